@@ -1,0 +1,252 @@
+"""The method, written out plainly in float64 (test infrastructure only).
+
+Sources (page titles as printed on the pages):
+
+* "Fuse shared-length query scaling during inference" -- Problem identified:
+  LogScale multiplies queries by a per-head coefficient times the log of a
+  shared key length; GatedLogScale adds a tanh gate through separate tanh,
+  addition and multiplication passes.  Solution: the length arithmetic is
+  float32 and every eager dtype-rounding boundary is preserved.  Summary
+  (sequence diagram): the eager path applies *clamped* log scaling.
+* "[FP8 3/4] Integrate FP8 attention and caching into TabICLv2" -- intro:
+  Q/K/V of intermediate ICL layers are quantised to FP8 above 8,192 unmasked
+  context rows; Q scales are derived from the context so cached prediction
+  does not depend on how queries are batched; ``model.fit`` builds the cache
+  and ``model.predict`` reuses it; shared attention projects Q/K/V and falls
+  back to SDPA (scaled dot-product attention, scale 1/sqrt(head_dim)).
+
+Readings where the pages are silent (each is a choice, listed with its
+reason in the design notes of the repository):
+
+* length: ``L32 = fp32(ln(max(n, 1)))`` (natural log; the clamp makes n <= 1
+  give 0); the per-head factor is ``k_h = fp16(fp32(L32 * c_h))``.
+* LogScale: ``q~ = fp16(q * k_h)``.  GatedLogScale:
+  ``q~ = fp16(fp16(q * k_h) * fp16(1 + fp16(tanh g)))`` with one gate value
+  per row and head.
+* FP8 scales per (batch, head) from the amax over valid rows: ``s = fp32(a /
+  448)``, ``inv = fp32(448 / a)`` (a = 0 gives s = inv = 1); codes are
+  ``e4m3(clamp(fp32(x * inv), +-448))``.  The Q scale comes from the *scaled*
+  context queries; query rows reuse it (and saturate above it).
+* masked context rows (index >= n) are not keys, not part of n and not part
+  of any amax; their outputs are zero.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+
+from .numerics import E4M3_MAX, E4M3_VALUES, e4m3_encode, e4m3_round
+
+SCALE_NONE, SCALE_LOG, SCALE_GATED_LOG = 0, 1, 2
+PREC_FP16, PREC_FP8_E4M3, PREC_AUTO = 0, 1, 2
+FP8_MIN_CONTEXT_ROWS = 8192
+
+
+# ---------------------------------------------------------------------------
+# Shared-length query scaling ("Fuse shared-length query scaling during
+# inference": Problem identified, Solution)
+# ---------------------------------------------------------------------------
+
+def length_scalar(n: int) -> np.float32:
+    """float32 log of the shared key length, clamped so that n <= 1 gives 0."""
+    return np.float32(math.log(max(int(n), 1)))
+
+
+def head_factors(L32: np.float32, head_coef: np.ndarray) -> np.ndarray:
+    """Per-head factor in float32 (length x coefficient), then converted to fp16."""
+    return (np.float32(L32) * np.asarray(head_coef, dtype=np.float32)).astype(np.float16)
+
+
+def gate_factor(gate: np.ndarray) -> np.ndarray:
+    """fp16(1 + fp16(tanh g)), each pass rounded to fp16 as in eager fp16 code."""
+    t = np.tanh(np.asarray(gate, dtype=np.float16).astype(np.float64)).astype(np.float16)
+    return (np.float32(1.0) + t.astype(np.float32)).astype(np.float16)
+
+
+def scale_queries(q: np.ndarray, mode: int, k_h: Optional[np.ndarray],
+                  gate: Optional[np.ndarray] = None) -> np.ndarray:
+    """Scaled query rows q~ (fp16) for q ``[..., H, D]`` and gate ``[..., H]``.
+
+    NONE leaves q unchanged; LOG multiplies by k_h with one fp16 rounding
+    (the product of two fp16 numbers is exact in float32); GATED further
+    multiplies by the gate factor with one more fp16 rounding.
+    """
+    q = np.asarray(q, dtype=np.float16)
+    if mode == SCALE_NONE:
+        return q.copy()
+    kh = np.asarray(k_h, dtype=np.float16).astype(np.float32)[:, None]
+    qk = (q.astype(np.float32) * kh).astype(np.float16)
+    if mode == SCALE_LOG:
+        return qk
+    if mode != SCALE_GATED_LOG:
+        raise ValueError(f"unknown scale mode {mode}")
+    u = gate_factor(gate).astype(np.float32)[..., None]
+    return (qk.astype(np.float32) * u).astype(np.float16)
+
+
+# ---------------------------------------------------------------------------
+# FP8 e4m3 quantisation with per-head, context-derived scales ("[FP8 3/4]
+# Integrate FP8 attention and caching into TabICLv2", introduction)
+# ---------------------------------------------------------------------------
+
+def select_precision(n: int, requested: int) -> int:
+    """FP8 only above 8,192 unmasked context rows when precision is automatic."""
+    if requested == PREC_AUTO:
+        return PREC_FP8_E4M3 if n > FP8_MIN_CONTEXT_ROWS else PREC_FP16
+    return requested
+
+
+def fp8_scale(amax) -> tuple:
+    """(s, inv) in float32 for one tensor's amax: s = a/448, inv = 448/a; a = 0 -> 1."""
+    a = np.float32(amax)
+    if a == 0:
+        return np.float32(1.0), np.float32(1.0)
+    return np.float32(a / np.float32(E4M3_MAX)), np.float32(np.float32(E4M3_MAX) / a)
+
+
+def amax_rows(x: np.ndarray) -> np.ndarray:
+    """max |x| over rows and head_dim for x ``[rows, H, D]`` -> ``[H]`` (fp16-exact)."""
+    return np.max(np.abs(x.astype(np.float64)), axis=(0, 2))
+
+
+def quantize(x: np.ndarray, inv) -> np.ndarray:
+    """E4M3 values (float64 on the grid) of fp16 x scaled by the float32 inverse scale."""
+    y = np.asarray(x, dtype=np.float16).astype(np.float32) * np.float32(inv)
+    y = np.clip(y.astype(np.float32), -E4M3_MAX, E4M3_MAX)
+    return e4m3_round(y)
+
+
+def quantize_codes(x: np.ndarray, inv) -> np.ndarray:
+    """E4M3 bit patterns of :func:`quantize`."""
+    return e4m3_encode(quantize(x, inv))
+
+
+# ---------------------------------------------------------------------------
+# Attention (SDPA semantics, non-causal): O_i = sum_j softmax_j(tau q_i.k_j) v_j
+# ---------------------------------------------------------------------------
+
+def attention_rows(qhat: np.ndarray, khat: np.ndarray, vhat: np.ndarray,
+                   tau: float) -> np.ndarray:
+    """Exact softmax attention of each query row over all given keys, float64.
+
+    ``qhat [m, D]``, ``khat [n, D]``, ``vhat [n, D]``.  Two passes per row:
+    the logits' maximum, then exp-weights normalised by their sum.
+    """
+    q = np.asarray(qhat, dtype=np.float64)
+    k = np.asarray(khat, dtype=np.float64)
+    v = np.asarray(vhat, dtype=np.float64)
+    z = (q @ k.T) * tau
+    z -= z.max(axis=1, keepdims=True)
+    p = np.exp(z)
+    return (p @ v) / p.sum(axis=1, keepdims=True)
+
+
+# ---------------------------------------------------------------------------
+# fit / predict, as on the TabICLv2 FP8 page (model.fit builds per-layer
+# caches, model.predict reuses them)
+# ---------------------------------------------------------------------------
+
+@dataclass
+class OracleCache:
+    """What ``fit`` keeps: the key length, scaling factors and the K/V operands."""
+
+    n: int
+    heads: int
+    head_dim: int
+    scale_mode: int
+    precision: int
+    L32: np.float32
+    k_h: Optional[np.ndarray]        # fp16 [H] or None
+    scales: np.ndarray               # float32 [3, B, H]: s_q, s_k, s_v (ones for FP16)
+    inv: np.ndarray                  # float32 [3, B, H]
+    k16: np.ndarray                  # fp16 [B, n, H, D] (valid rows only)
+    v16: np.ndarray
+    k_codes: Optional[np.ndarray]    # uint8 [B, H, n, D] (FP8 only)
+    v_codes: Optional[np.ndarray]
+
+    @property
+    def tau(self) -> float:
+        return 1.0 / math.sqrt(self.head_dim)
+
+    def khat(self, b: int, h: int) -> np.ndarray:
+        if self.precision == PREC_FP8_E4M3:
+            return E4M3_VALUES[self.k_codes[b, h]] * np.float64(self.scales[1, b, h])
+        return self.k16[b, :, h, :].astype(np.float64)
+
+    def vhat(self, b: int, h: int) -> np.ndarray:
+        if self.precision == PREC_FP8_E4M3:
+            return E4M3_VALUES[self.v_codes[b, h]] * np.float64(self.scales[2, b, h])
+        return self.v16[b, :, h, :].astype(np.float64)
+
+    def qhat(self, qt: np.ndarray, b: int, h: int) -> np.ndarray:
+        """Operand used for scaled query rows qt ``[m, H, D]`` (fp16) of head h."""
+        x = qt[:, h, :]
+        if self.precision == PREC_FP8_E4M3:
+            return quantize(x, self.inv[0, b, h]) * np.float64(self.scales[0, b, h])
+        return x.astype(np.float64)
+
+
+def fit(q: np.ndarray, k: np.ndarray, v: np.ndarray, n: int, scale_mode: int,
+        precision: int, head_coef: Optional[np.ndarray] = None,
+        gate: Optional[np.ndarray] = None, keep_codes: bool = True) -> OracleCache:
+    """Build the cache from context Q/K/V ``[B, N_pad, H, D]`` with n valid rows."""
+    B, N, H, D = q.shape
+    if not 1 <= n <= N:
+        raise ValueError("need 1 <= n <= N_pad")
+    prec = select_precision(n, precision)
+    L32 = length_scalar(n)
+    k_h = head_factors(L32, head_coef) if scale_mode != SCALE_NONE else None
+    scales = np.ones((3, B, H), dtype=np.float32)
+    inv = np.ones((3, B, H), dtype=np.float32)
+    k_codes = v_codes = None
+    if prec == PREC_FP8_E4M3:
+        k_codes = np.empty((B, H, n, D), dtype=np.uint8)
+        v_codes = np.empty((B, H, n, D), dtype=np.uint8)
+        for b in range(B):
+            qt = scale_queries(q[b, :n], scale_mode, k_h,
+                               None if gate is None else gate[b, :n])
+            for t, x in enumerate((qt, k[b, :n], v[b, :n])):
+                a = amax_rows(x)
+                for h in range(H):
+                    scales[t, b, h], inv[t, b, h] = fp8_scale(a[h])
+            for h in range(H):
+                k_codes[b, h] = quantize_codes(k[b, :n, h, :], inv[1, b, h])
+                v_codes[b, h] = quantize_codes(v[b, :n, h, :], inv[2, b, h])
+    return OracleCache(n=n, heads=H, head_dim=D, scale_mode=scale_mode, precision=prec,
+                       L32=L32, k_h=k_h, scales=scales, inv=inv,
+                       k16=k[:, :n], v16=v[:, :n], k_codes=k_codes, v_codes=v_codes)
+
+
+def attend(cache: OracleCache, q_rows: np.ndarray, gate_rows: Optional[np.ndarray],
+           b: int = 0, heads: Optional[Sequence[int]] = None,
+           block: int = 128) -> np.ndarray:
+    """Outputs (float64 ``[m, H, D]``) of query rows ``q_rows [m, H, D]`` of batch b.
+
+    Rows are scaled with the cache's length and coefficients, quantised with
+    the cache's context-derived Q scale in FP8 mode, and attend to all n keys.
+    Rows are evaluated independently, ``block`` at a time to bound memory.
+    """
+    qt = scale_queries(q_rows, cache.scale_mode, cache.k_h, gate_rows)
+    m = q_rows.shape[0]
+    out = np.zeros((m, cache.heads, cache.head_dim), dtype=np.float64)
+    for h in (range(cache.heads) if heads is None else heads):
+        kh, vh = cache.khat(b, h), cache.vhat(b, h)
+        qh = cache.qhat(qt, b, h)
+        for r0 in range(0, m, block):
+            out[r0:r0 + block, h] = attention_rows(qh[r0:r0 + block], kh, vh, cache.tau)
+    return out
+
+
+def context_outputs(cache: OracleCache, q: np.ndarray, gate: Optional[np.ndarray],
+                    rows: Sequence[int], b: int = 0, heads=None) -> np.ndarray:
+    """Self-attention outputs of the given context rows (masked rows give 0)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.zeros((rows.size, cache.heads, cache.head_dim), dtype=np.float64)
+    valid = rows < cache.n
+    if np.any(valid):
+        g = None if gate is None else gate[b, rows[valid]]
+        out[valid] = attend(cache, q[b, rows[valid]], g, b=b, heads=heads)
+    return out

@@ -1,0 +1,290 @@
+"""Pins of the float64 oracle to facts outside itself (CPU only).
+
+Each test checks the oracle against something it does not compute itself: the
+OCP E4M3 code table, torch's own E4M3 cast, closed forms of softmax attention,
+hand-derived scaling examples, and a second, loop-based formulation of the
+attention sum on tiny inputs.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import icl, numerics
+from long_context_tabular_amd import inputs as gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _all_finite_fp16():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = bits.view(np.float16)
+    return v[np.isfinite(v)]
+
+
+# --------------------------------------------------------------------------- e4m3
+
+def test_e4m3_code_points_match_ocp_table():
+    rows = []
+    with open(os.path.join(GOLDEN, "e4m3_code_points.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                code, val = line.split()
+                rows.append((int(code, 16), float(val)))
+    table = numerics.E4M3_VALUES
+    for code, val in rows:
+        if math.isnan(val):
+            assert math.isnan(table[code])
+            continue
+        assert table[code] == val and math.copysign(1, table[code]) == math.copysign(1, val)
+        assert numerics.e4m3_encode(np.array([val]))[0] == code
+        assert numerics.e4m3_round(np.array([val]))[0] == val
+
+
+def test_e4m3_round_matches_torch_cast_on_all_fp16_values():
+    """torch's CPU float8_e4m3fn cast rounds to nearest even; it does not
+    saturate, so both sides see values already clamped to +-448."""
+    v = _all_finite_fp16().astype(np.float32)
+    for scale in (1.0, 7.0, 448.0 / 2.5, 1.0 / 3.0, 2.0 ** -7, 1000.0):
+        x = np.clip(v * np.float32(scale), -448, 448).astype(np.float32)
+        ours = numerics.e4m3_round(x)
+        ref = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+        np.testing.assert_array_equal(ours, ref)
+        codes = numerics.e4m3_encode(ours)
+        ref_codes = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        np.testing.assert_array_equal(codes, ref_codes)
+
+
+def test_e4m3_ties_go_to_even_and_error_is_at_most_half_spacing():
+    # 1 + 1/16 lies halfway between 1.0 (mantissa 0) and 1.125 (mantissa 1)
+    assert numerics.e4m3_round(np.array([1.0625]))[0] == 1.0
+    # 1 + 3/16 lies halfway between 1.125 (odd) and 1.25 (even)
+    assert numerics.e4m3_round(np.array([1.1875]))[0] == 1.25
+    # 432 lies halfway between 416 (mantissa 5) and 448 (mantissa 6)
+    assert numerics.e4m3_round(np.array([432.0]))[0] == 448.0
+    # subnormal tie: 1.5 * 2^-9 goes to 2 * 2^-9
+    assert numerics.e4m3_round(np.array([1.5 * 2.0 ** -9]))[0] == 2.0 * 2.0 ** -9
+    x = np.random.default_rng(5).uniform(-448, 448, 200000)
+    r = numerics.e4m3_round(x)
+    a = np.maximum(np.abs(x), 2.0 ** -6)
+    spacing = 2.0 ** (np.floor(np.log2(a)) - 3)
+    assert np.all(np.abs(r - x) <= spacing / 2 + 1e-300)
+    assert np.all(np.diff(numerics.e4m3_round(np.sort(x))) >= 0)
+
+
+def test_e4m3_rejects_unclamped_values():
+    with pytest.raises(ValueError):
+        numerics.e4m3_round(np.array([500.0]))
+
+
+# --------------------------------------------------------------------------- scaling
+
+def test_length_scalar_closed_forms():
+    # ln(2^k) = k ln 2; the clamp makes n = 0 and n = 1 give 0.
+    for k in range(0, 21):
+        assert icl.length_scalar(2 ** k) == np.float32(k * math.log(2.0))
+    assert icl.length_scalar(0) == 0.0 and icl.length_scalar(1) == 0.0
+    assert icl.length_scalar(16384).dtype == np.float32
+    # float32 rounding of the natural log (not log2 / log10)
+    assert abs(float(icl.length_scalar(523288)) - math.log(523288)) < 2 ** -20 * 13.2
+    assert abs(float(icl.length_scalar(1000)) - 6.907755278982137) < 1e-6
+
+
+def test_head_factor_and_identity_scalings():
+    L = icl.length_scalar(16384)
+    coef = np.array([np.float32(1.0) / L, np.float32(2.0) / L], dtype=np.float32)
+    kh = icl.head_factors(L, coef)
+    assert kh.dtype == np.float16 and kh[0] == 1.0 and kh[1] == 2.0
+    q = gen.make_inputs(gen.scaled_down(gen.WORKLOADS["tiny_fp16"], 64)).q_ctx[0, :, :2]
+    # k_h = 1 leaves q unchanged; k_h = 2 doubles it exactly
+    np.testing.assert_array_equal(icl.scale_queries(q, icl.SCALE_LOG, np.array([1, 1], np.float16)), q)
+    np.testing.assert_array_equal(icl.scale_queries(q, icl.SCALE_LOG, np.array([2, 2], np.float16)),
+                                  (q.astype(np.float32) * 2).astype(np.float16))
+    np.testing.assert_array_equal(icl.scale_queries(q, icl.SCALE_NONE, None), q)
+    # a zero gate reduces GatedLogScale to LogScale
+    g0 = np.zeros(q.shape[:2], np.float16)
+    kh2 = np.array([1.5, 0.75], np.float16)
+    np.testing.assert_array_equal(icl.scale_queries(q, icl.SCALE_GATED_LOG, kh2, g0),
+                                  icl.scale_queries(q, icl.SCALE_LOG, kh2))
+
+
+def test_scaling_worked_examples():
+    with open(os.path.join(GOLDEN, "scaling_worked_examples.txt")) as f:
+        rows = [list(map(float, l.split())) for l in f if l.strip() and not l.startswith("#")]
+    assert len(rows) == 5
+    for q, kh, g, want in rows:
+        out = icl.scale_queries(np.array([[[q]]], np.float16), icl.SCALE_GATED_LOG,
+                                np.array([kh], np.float16), np.array([[g]], np.float16))
+        assert out.dtype == np.float16 and float(out[0, 0, 0]) == want, (q, kh, g, out)
+
+
+def test_gate_factor_over_every_fp16_gate():
+    g = _all_finite_fp16()
+    u = icl.gate_factor(g).astype(np.float64)
+    assert np.all((u >= 0) & (u <= 2))
+    order = np.argsort(g.astype(np.float64), kind="stable")
+    assert np.all(np.diff(u[order]) >= 0)           # 1 + tanh is non-decreasing
+    # tanh(g) of an fp16 g rounds to the fp16 nearest the exact value
+    t = np.tanh(g.astype(np.float64)).astype(np.float16)
+    assert np.all(np.abs(t.astype(np.float64) - np.tanh(g.astype(np.float64)))
+                  <= np.spacing(np.abs(t).astype(np.float16)).astype(np.float64) / 2 + 1e-12)
+
+
+# --------------------------------------------------------------------------- fp8 scales
+
+def test_fp8_scale_maps_amax_to_448_and_bounds_error():
+    x = gen.make_inputs(gen.scaled_down(gen.WORKLOADS["ctx128k_fp8"], 4096)).k_ctx[0, :, 0, :]
+    a = float(np.max(np.abs(x.astype(np.float64))))
+    s, inv = icl.fp8_scale(a)
+    assert s.dtype == np.float32 and s == np.float32(np.float32(a) / np.float32(448))
+    vals = icl.quantize(x, inv)
+    assert np.max(np.abs(vals)) == 448.0
+    idx = np.unravel_index(np.argmax(np.abs(x.astype(np.float64))), x.shape)
+    assert abs(vals[idx]) == 448.0
+    deq = vals * np.float64(s)
+    ref = x.astype(np.float64)
+    big = np.abs(ref) >= 2.0 ** -6 * float(s)
+    assert np.all(np.abs(deq - ref)[big] <= np.abs(ref)[big] * 2.0 ** -4 * (1 + 1e-6))
+    # an all-zero tensor gets unit scales and zero codes
+    s0, inv0 = icl.fp8_scale(0.0)
+    assert s0 == 1.0 and inv0 == 1.0
+    # values above the context amax saturate
+    assert icl.quantize(np.array([a * 4], np.float16), inv)[0] == 448.0
+
+
+def test_precision_auto_threshold():
+    assert icl.select_precision(8192, icl.PREC_AUTO) == icl.PREC_FP16
+    assert icl.select_precision(8193, icl.PREC_AUTO) == icl.PREC_FP8_E4M3
+    assert icl.select_precision(100, icl.PREC_FP8_E4M3) == icl.PREC_FP8_E4M3
+
+
+# --------------------------------------------------------------------------- attention
+
+def _loop_attention(q, k, v, tau):
+    """Second formulation: per-row log-sum-exp with math.fsum, plain Python loops."""
+    out = []
+    for qi in q:
+        logits = [tau * math.fsum(float(a) * float(b) for a, b in zip(qi, kj)) for kj in k]
+        m = max(logits)
+        lse = m + math.log(math.fsum(math.exp(z - m) for z in logits))
+        w = [math.exp(z - lse) for z in logits]
+        out.append([math.fsum(wj * float(vj[d]) for wj, vj in zip(w, v)) for d in range(len(v[0]))])
+    return np.array(out)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 17, 63, 64, 65, 127, 128, 129])
+def test_attention_brute_force_tiny(n):
+    rng = np.random.default_rng(n)
+    D = 8
+    q = rng.standard_normal((7, D)) * 1.5
+    k = rng.standard_normal((n, D))
+    v = rng.standard_normal((n, D))
+    got = icl.attention_rows(q, k, v, 1 / math.sqrt(D))
+    np.testing.assert_allclose(got, _loop_attention(q, k, v, 1 / math.sqrt(D)), rtol=1e-12, atol=1e-13)
+
+
+def test_attention_closed_forms():
+    rng = np.random.default_rng(11)
+    D, n = 64, 300
+    q = rng.standard_normal((5, D))
+    k = rng.standard_normal((n, D))
+    v = rng.standard_normal((n, D))
+    tau = 1 / 8
+    # I1: constant V -> output is that constant (weights sum to one)
+    np.testing.assert_allclose(icl.attention_rows(q, k, np.full((n, D), 0.375), tau), 0.375, rtol=0, atol=1e-15)
+    # I2: a single key -> output is its value row
+    np.testing.assert_allclose(icl.attention_rows(q, k[:1], v[:1], tau), np.repeat(v[:1], 5, 0), atol=1e-15)
+    # I3: identical keys -> the mean of V
+    np.testing.assert_allclose(icl.attention_rows(q, np.repeat(k[:1], n, 0), v, tau),
+                               np.repeat(v.mean(0, keepdims=True), 5, 0), atol=1e-14)
+    # two keys with logits ln 3 and 0 (tau = 1/8): weights 3/4 and 1/4
+    qq = np.zeros((1, D)); qq[0, 0] = 1.0
+    kk = np.zeros((2, D)); kk[0, 0] = 8 * math.log(3.0)
+    vv = rng.standard_normal((2, D))
+    np.testing.assert_allclose(icl.attention_rows(qq, kk, vv, tau)[0], 0.75 * vv[0] + 0.25 * vv[1], atol=1e-14)
+    # a large shift of every logit (softmax shift invariance) changes nothing
+    kk2 = kk + 0.0
+    kk2[:, 1] = 1e3
+    qq2 = qq.copy(); qq2[0, 1] = 1.0
+    np.testing.assert_allclose(icl.attention_rows(qq2, kk2, vv, tau)[0], 0.75 * vv[0] + 0.25 * vv[1], atol=1e-12)
+
+
+# --------------------------------------------------------------------------- fit / attend
+
+def _small(name, n_pad, n_valid=None, n_query=16):
+    return gen.make_inputs(gen.scaled_down(gen.WORKLOADS[name], n_pad, n_valid, n_query))
+
+
+def test_masked_rows_are_ignored():
+    x = _small("model512k_fp8_log", 2048, 1500)
+    assert np.isnan(x.k_ctx[0, 1600]).all()
+    args = dict(scale_mode=icl.SCALE_LOG, precision=icl.PREC_FP8_E4M3, head_coef=x.head_coef)
+    c1 = icl.fit(x.q_ctx, x.k_ctx, x.v_ctx, 1500, **args)
+    c2 = icl.fit(x.q_ctx[:, :1500].copy(), x.k_ctx[:, :1500].copy(), x.v_ctx[:, :1500].copy(), 1500, **args)
+    np.testing.assert_array_equal(c1.scales, c2.scales)
+    np.testing.assert_array_equal(c1.k_codes, c2.k_codes)
+    assert c1.L32 == icl.length_scalar(1500)
+    rows = [0, 7, 1499, 1500, 2047]
+    o = icl.context_outputs(c1, x.q_ctx, None, rows, heads=[0, 3])
+    assert np.all(np.isfinite(o))
+    assert np.all(o[3:] == 0)
+
+
+def test_fp8_is_lossless_on_grid_inputs():
+    """I10: when Q~, K, V already lie on the e4m3 grid with amax = 448 s, FP8
+    quantisation changes nothing and the FP8 result equals the FP16 one.  Each
+    tensor and head gets its own power-of-two scale so that a mixed-up scale
+    (s_k used for V, say) changes the result."""
+    rng = np.random.default_rng(3)
+    B, N, H, D = 1, 96, 2, 64
+    grid = numerics.E4M3_VALUES[np.isfinite(numerics.E4M3_VALUES)]
+    grid = grid[np.abs(grid) <= 64]
+    scales = {"q": (2.0 ** -9, 2.0 ** -8), "k": (2.0 ** -10, 2.0 ** -7), "v": (2.0 ** -6, 2.0 ** -11)}
+    def draw(name):
+        t = np.empty((B, N, H, D))
+        for h in range(H):
+            s = scales[name][h]
+            t[0, :, h] = rng.choice(grid, size=(N, D)) * s
+            t[0, 0, h, 0] = 448 * s          # pin amax to 448 s in every head
+        assert np.all(t.astype(np.float16).astype(np.float64) == t)   # fp16-exact
+        return t.astype(np.float16)
+    q, k, v = draw("q"), draw("k"), draw("v")
+    c8 = icl.fit(q, k, v, N, icl.SCALE_NONE, icl.PREC_FP8_E4M3)
+    c16 = icl.fit(q, k, v, N, icl.SCALE_NONE, icl.PREC_FP16)
+    for t, name in enumerate("qkv"):
+        np.testing.assert_array_equal(c8.scales[t, 0], np.float32(scales[name]))
+    rows = np.arange(N)
+    ref = icl.context_outputs(c16, q, None, rows)
+    np.testing.assert_allclose(icl.context_outputs(c8, q, None, rows), ref,
+                               rtol=0, atol=1e-15 * np.abs(ref).max())
+
+
+def test_query_rows_use_context_q_scale():
+    x = _small("cached512k_fp8_gated", 1024, n_query=32)
+    c = icl.fit(x.q_ctx, x.k_ctx, x.v_ctx, 1024, icl.SCALE_GATED_LOG, icl.PREC_FP8_E4M3,
+                x.head_coef, x.gate_ctx)
+    qt = icl.scale_queries(x.q_ctx[0], icl.SCALE_GATED_LOG, c.k_h, x.gate_ctx[0])
+    for h in range(x.workload.heads):
+        a = np.max(np.abs(qt[:, h].astype(np.float64)))
+        assert c.scales[0, 0, h] == icl.fp8_scale(a)[0]
+    # splitting queries into batches cannot change any row
+    full = icl.attend(c, x.q_query[0], x.gate_query[0], heads=[1])
+    half = np.concatenate([icl.attend(c, x.q_query[0, :16], x.gate_query[0, :16], heads=[1]),
+                           icl.attend(c, x.q_query[0, 16:], x.gate_query[0, 16:], heads=[1])])
+    np.testing.assert_array_equal(full, half)
+
+
+def test_inputs_recipe():
+    w = gen.scaled_down(gen.WORKLOADS["ctx128k_fp8"], 65536, n_query=8)
+    x = gen.make_inputs(w)
+    k = x.k_ctx.astype(np.float64)
+    frac = np.mean(np.abs(k) == 2.5)
+    assert 5e-4 < frac < 2e-3
+    core = k[np.abs(k) != 2.5]
+    assert abs(core.std() - 0.125) < 2e-3
+    assert x.k_ctx.dtype == np.float16 and x.head_coef.dtype == np.float32
+    assert np.all((x.head_coef >= 0.5) & (x.head_coef <= 1.5))
+    y = gen.make_inputs(w)
+    np.testing.assert_array_equal(x.q_query, y.q_query)
