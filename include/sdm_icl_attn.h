@@ -1,0 +1,193 @@
+/*
+ * sdm_icl_attn.h -- C ABI of the MI355X (gfx950) row-wise in-context-learning
+ * (ICL) attention engine of tabular foundation models.
+ *
+ * What it computes
+ * ----------------
+ * Context rows are tokens that attend to one another without a causal mask;
+ * query rows attend to the context keys/values only, either in the same call
+ * or later from a cached K/V ("[FP8 3/4] Integrate FP8 attention and caching
+ * into TabICLv2": model(context, labels, queries), model.fit(context, labels)
+ * then model.predict(queries); shared attention projects Q/K/V and falls back
+ * to scaled dot-product attention).  For a query row i:
+ *
+ *     O_i = sum_{j < n} softmax_j( (q~_i . k_j) / sqrt(D) ) v_j
+ *
+ * where n is the number of valid (unmasked) context rows and q~ is the query
+ * after the optional shared-length scaling ("Fuse shared-length query scaling
+ * during inference", Problem identified / Solution):
+ *
+ *     NONE       q~ = q
+ *     LOG        q~ = fp16(q * k_h)          k_h = fp16(fp32(L32 * c_h))
+ *     GATED_LOG  q~ = fp16(fp16(q * k_h) * fp16(1 + fp16(tanh g)))
+ *     L32 = fp32(ln(max(n, 1)))   (float32 length arithmetic, clamped log)
+ *
+ * With FP8 precision ("[FP8 3/4] ...", introduction) Q~, K and V are
+ * quantised to OCP e4m3 with per-(batch, head) scales s = amax/448 taken over
+ * the valid context rows (for Q, over the *scaled context* queries), codes =
+ * e4m3_rne(clamp(fp32(x * (448/amax)), -448, 448)).  Query rows reuse the
+ * context's Q scale, so a row's result does not depend on how the queries are
+ * split into batches.  Softmax and accumulation are fp32; outputs are fp16.
+ *
+ * Conventions (all entry points)
+ * ------------------------------
+ * - Pointers named "device" are HIP device memory on the stream's device and
+ *   stay owned by the caller; "host" pointers are read during the call only.
+ * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *   All device work is enqueued on it; no entry point synchronises the host
+ *   unless stated (cache_export does).
+ * - Every argument is validated on the host before anything is launched; a
+ *   non-OK status leaves outputs untouched and sdm_icl_last_error() holds a
+ *   message for the calling thread.  Errors of already-launched kernels show
+ *   up as SDM_ICL_E_HIP from a later call or at the caller's next sync.
+ * - head_dim must be 64 (the ICL width of the models on the pages is 8 x 64);
+ *   other values return SDM_ICL_E_UNSUPPORTED.
+ * - Only gfx950 devices are supported (SDM_ICL_E_DEVICE otherwise).
+ */
+#ifndef SDM_ICL_ATTN_H
+#define SDM_ICL_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t sdm_icl_status;
+#define SDM_ICL_OK            0
+#define SDM_ICL_E_INVALID     1  /* bad argument: null pointer, size, mode/gate mismatch */
+#define SDM_ICL_E_UNSUPPORTED 2  /* valid but not implemented (head_dim != 64, per-batch lengths) */
+#define SDM_ICL_E_DEVICE      3  /* pointer not on the stream's device, or not a gfx950 device */
+#define SDM_ICL_E_OOM         4  /* device allocation failed */
+#define SDM_ICL_E_HIP         5  /* a HIP runtime call failed */
+#define SDM_ICL_E_STATE       6  /* released or unknown cache handle; workspace too small */
+
+#define SDM_ICL_SCALE_NONE      0
+#define SDM_ICL_SCALE_LOG       1
+#define SDM_ICL_SCALE_GATED_LOG 2
+
+#define SDM_ICL_PREC_FP16     0
+#define SDM_ICL_PREC_FP8_E4M3 1
+#define SDM_ICL_PREC_AUTO     2  /* FP8 iff n > 8192 valid context rows ("[FP8 3/4] ...", intro) */
+
+/* Opaque, library-owned, immutable after fit.  Holds n, the scaling factors,
+ * the per-head FP8 scales and the K/V operands in a head-major layout. */
+typedef struct sdm_icl_cache_s* sdm_icl_cache;
+
+typedef struct {
+  int32_t batch;           /* B >= 1 */
+  int32_t rows_padded;     /* N_pad >= 1: allocated context rows per batch element */
+  int32_t heads;           /* H, 1..128 */
+  int32_t head_dim;        /* D, must be 64 */
+  const int64_t* lengths;  /* host [B]: valid rows n_b, 1 <= n_b <= N_pad; all equal (one
+                              shared length, as the fused scaling path requires); rows
+                              n..N_pad-1 are masked: not keys, not in n, not in any amax,
+                              their outputs are 0 and their contents are never read */
+  const void* q;           /* device fp16 [B, N_pad, H, D], row-major, row stride H*D */
+  const void* k;           /* device fp16 [B, N_pad, H, D] */
+  const void* v;           /* device fp16 [B, N_pad, H, D] */
+  const void* gate;        /* device fp16 [B, N_pad, H]; non-NULL iff scale_mode == GATED_LOG */
+  const float* head_coef;  /* host float32 [H] (c_h); non-NULL iff scale_mode != NONE */
+  int32_t scale_mode;      /* SDM_ICL_SCALE_* */
+  int32_t precision;       /* SDM_ICL_PREC_* */
+  void* out_ctx;           /* device fp16 [B, N_pad, H, D] context self-attention output,
+                              or NULL to only build the cache (model.fit) */
+  void* stream;            /* hipStream_t */
+} sdm_icl_fit_args;
+
+typedef struct {
+  int32_t batch, heads, head_dim;
+  int32_t precision;       /* resolved: FP16 or FP8_E4M3, never AUTO */
+  int32_t scale_mode;
+  int32_t kv_splits;       /* KV-axis split count used by every query call (fixed at fit) */
+  int64_t n_valid;         /* n */
+  int64_t rows_alloc;      /* cache rows per (b, h): n rounded up to the 64-row key tile */
+  int64_t keys_per_split;  /* rows of each KV split (multiple of 64) */
+  float length_scalar;     /* L32 */
+  uint64_t device_bytes;   /* bytes of device memory the cache holds */
+} sdm_icl_cache_info;
+
+/* Build the K/V cache from the context (model.fit) and, if out_ctx != NULL,
+ * also compute the context rows' self-attention (the context half of one
+ * model call).  Allocates the cache with stream-ordered allocation on
+ * args->stream; *out receives the handle only on SDM_ICL_OK.  Temporary
+ * buffers of the call are freed stream-ordered before it returns. */
+sdm_icl_status sdm_icl_attn_fit(const sdm_icl_fit_args* args, sdm_icl_cache* out);
+
+/* Device workspace (bytes) that sdm_icl_attn_query needs for n_query rows:
+ * fp32 split partials (m, l and an unnormalised O row per KV split). */
+sdm_icl_status sdm_icl_attn_query_workspace_size(sdm_icl_cache cache, int64_t n_query,
+                                                 size_t* bytes);
+
+/* Query rows attend to the cached context (model.predict).  q: device fp16
+ * [B, R, H, D]; gate: device fp16 [B, R, H], non-NULL iff the cache was fitted
+ * with GATED_LOG (otherwise SDM_ICL_E_INVALID, the analogue of misusing an FP8
+ * cache outside its scope); out: device fp16 [B, R, H, D].  workspace: caller
+ * device memory of at least query_workspace_size(R) bytes.  Allocates nothing
+ * and never synchronises.  The result of a row is bitwise independent of R
+ * and of the other rows in the call (fixed KV split plan, fixed combine
+ * order, context-derived Q scale).  R == 0 is a no-op.  Concurrent calls on
+ * one cache with distinct workspaces are safe. */
+sdm_icl_status sdm_icl_attn_query(sdm_icl_cache cache, const void* q, const void* gate,
+                                  int64_t n_query, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* Shape, precision and split plan of a cache. */
+sdm_icl_status sdm_icl_attn_cache_info(sdm_icl_cache cache, sdm_icl_cache_info* info);
+
+/* Copy the cached operands to host memory (parity checks, persistence).
+ * host_k / host_v: [B, H, n, D] elements, 1 byte (e4m3 code) in FP8 mode or
+ * 2 bytes (fp16) in FP16 mode; host_scales: float32 [3, B, H] = s_q, s_k, s_v
+ * (all 1 in FP16 mode).  Any of the three may be NULL.  Synchronises `stream`. */
+sdm_icl_status sdm_icl_attn_cache_export(sdm_icl_cache cache, void* host_k, void* host_v,
+                                         float* host_scales, void* stream);
+
+/* Free a cache.  The memory is returned stream-ordered on the stream the cache
+ * was fitted on; work on other streams that uses the cache must be complete
+ * (or ordered before that stream) first.  A second release of the same handle
+ * returns SDM_ICL_E_STATE. */
+sdm_icl_status sdm_icl_attn_release(sdm_icl_cache cache);
+
+/* The fused shared-length query scaling on its own ("Fuse shared-length query
+ * scaling during inference", Solution: length preparation, per-head
+ * conversion, query multiplication and optional gating in one kernel).
+ * q: device fp16 [B, rows, H, D]; gate: device fp16 [B, rows, H] iff GATED_LOG;
+ * key_length: the shared n (>= 0; the log is clamped at n <= 1);
+ * head_coef: host float32 [H] unless NONE.  out: device, head-major
+ * [B, H, rows, D]: fp16 when q_inv_scale is NULL, else e4m3 codes (1 byte)
+ * of the scaled rows quantised with the device float32 inverse scales
+ * q_inv_scale [B, H] (448 / amax). */
+sdm_icl_status sdm_icl_log_scale(const void* q, const void* gate, int32_t batch, int64_t rows,
+                                 int32_t heads, int32_t head_dim, int64_t key_length,
+                                 const float* head_coef, int32_t scale_mode,
+                                 const float* q_inv_scale, void* out, void* stream);
+
+/* ---- host-only helpers (no device work; usable without a GPU) ---------- */
+
+/* L32 = fp32(ln(max(n, 1))). */
+float sdm_icl_length_scalar(int64_t n);
+
+/* k_h = fp16(fp32(L32(n) * c_h)) for h < heads, written as fp16 bit patterns. */
+sdm_icl_status sdm_icl_head_factors(int64_t n, const float* head_coef, int32_t heads,
+                                    uint16_t* out_fp16_bits);
+
+/* Precision a fit with this n and request resolves to (AUTO: FP8 iff n > 8192). */
+int32_t sdm_icl_select_precision(int64_t n, int32_t requested);
+
+/* KV split plan for n valid keys on a device with num_cus compute units:
+ * a pure function of (n, num_cus), never of the query count. */
+sdm_icl_status sdm_icl_split_plan(int64_t n, int32_t num_cus, int32_t* kv_splits,
+                                  int64_t* keys_per_split);
+
+/* Message of the last non-OK status on this thread ("" if none). */
+const char* sdm_icl_last_error(void);
+
+/* ABI version (major * 100 + minor). */
+int32_t sdm_icl_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDM_ICL_ATTN_H */

@@ -1,0 +1,280 @@
+"""Thin ctypes binding of ``include/sdm_icl_attn.h`` (argument marshalling only).
+
+Every step of the attention path runs in the HIP library; this module only
+checks tensor dtypes/devices, passes raw pointers and the current HIP stream,
+and turns non-OK status codes into exceptions.  There is no fallback: if
+``libsdm_icl_attn.so`` is missing the first call raises.
+
+Function names mirror the C ABI.  PyTorch is used for device memory and
+streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsdm_icl_attn.so")
+
+SDM_ICL_OK = 0
+STATUS_NAMES = {0: "OK", 1: "E_INVALID", 2: "E_UNSUPPORTED", 3: "E_DEVICE", 4: "E_OOM",
+                5: "E_HIP", 6: "E_STATE"}
+SDM_ICL_SCALE_NONE, SDM_ICL_SCALE_LOG, SDM_ICL_SCALE_GATED_LOG = 0, 1, 2
+SDM_ICL_PREC_FP16, SDM_ICL_PREC_FP8_E4M3, SDM_ICL_PREC_AUTO = 0, 1, 2
+
+
+class SdmIclError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class FitArgs(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("rows_padded", ctypes.c_int32),
+                ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("lengths", ctypes.POINTER(ctypes.c_int64)),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("gate", ctypes.c_void_p), ("head_coef", ctypes.POINTER(ctypes.c_float)),
+                ("scale_mode", ctypes.c_int32), ("precision", ctypes.c_int32),
+                ("out_ctx", ctypes.c_void_p), ("stream", ctypes.c_void_p)]
+
+
+class CacheInfo(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("precision", ctypes.c_int32), ("scale_mode", ctypes.c_int32),
+                ("kv_splits", ctypes.c_int32), ("n_valid", ctypes.c_int64),
+                ("rows_alloc", ctypes.c_int64), ("keys_per_split", ctypes.c_int64),
+                ("length_scalar", ctypes.c_float), ("device_bytes", ctypes.c_uint64)]
+
+
+# name -> (restype, argtypes), exactly the declarations of include/sdm_icl_attn.h
+_SIGNATURES = {
+    "sdm_icl_attn_fit": (ctypes.c_int32, [ctypes.POINTER(FitArgs), ctypes.POINTER(ctypes.c_void_p)]),
+    "sdm_icl_attn_query_workspace_size": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_int64,
+                                                           ctypes.POINTER(ctypes.c_size_t)]),
+    "sdm_icl_attn_query": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_size_t, ctypes.c_void_p]),
+    "sdm_icl_attn_cache_info": (ctypes.c_int32, [ctypes.c_void_p, ctypes.POINTER(CacheInfo)]),
+    "sdm_icl_attn_cache_export": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                   ctypes.c_void_p, ctypes.c_void_p]),
+    "sdm_icl_attn_release": (ctypes.c_int32, [ctypes.c_void_p]),
+    "sdm_icl_log_scale": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                           ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int64, ctypes.POINTER(ctypes.c_float),
+                                           ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_void_p]),
+    "sdm_icl_length_scalar": (ctypes.c_float, [ctypes.c_int64]),
+    "sdm_icl_head_factors": (ctypes.c_int32, [ctypes.c_int64, ctypes.POINTER(ctypes.c_float),
+                                              ctypes.c_int32, ctypes.POINTER(ctypes.c_uint16)]),
+    "sdm_icl_select_precision": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32]),
+    "sdm_icl_split_plan": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32,
+                                            ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]),
+    "sdm_icl_last_error": (ctypes.c_char_p, []),
+    "sdm_icl_version": (ctypes.c_int32, []),
+}
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m long_context_tabular_amd.build_lib` (or __graft_entry__.build())")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = handle
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != SDM_ICL_OK:
+        raise SdmIclError(status, lib().sdm_icl_last_error().decode())
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream or None
+
+
+def _dev_ptr(t, name: str, dtype=None) -> Optional[int]:
+    if t is None:
+        return None
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+# ------------------------------------------------------------------ host helpers
+
+def sdm_icl_version() -> int:
+    return lib().sdm_icl_version()
+
+
+def sdm_icl_last_error() -> str:
+    return lib().sdm_icl_last_error().decode()
+
+
+def sdm_icl_length_scalar(n: int) -> np.float32:
+    return np.float32(lib().sdm_icl_length_scalar(int(n)))
+
+
+def sdm_icl_head_factors(n: int, head_coef) -> np.ndarray:
+    coef = np.ascontiguousarray(head_coef, dtype=np.float32)
+    out = np.zeros(coef.size, dtype=np.uint16)
+    _check(lib().sdm_icl_head_factors(int(n), coef.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                                      coef.size, out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16))))
+    return out.view(np.float16)
+
+
+def sdm_icl_select_precision(n: int, requested: int) -> int:
+    return lib().sdm_icl_select_precision(int(n), int(requested))
+
+
+def sdm_icl_split_plan(n: int, num_cus: int):
+    s = ctypes.c_int32()
+    k = ctypes.c_int64()
+    _check(lib().sdm_icl_split_plan(int(n), int(num_cus), ctypes.byref(s), ctypes.byref(k)))
+    return s.value, k.value
+
+
+# ------------------------------------------------------------------ cache handle
+
+class Cache:
+    """Owns one ``sdm_icl_cache`` handle; ``release()`` frees it."""
+
+    def __init__(self, handle: int):
+        self.handle = handle
+
+    def info(self) -> dict:
+        return sdm_icl_attn_cache_info(self)
+
+    def release(self) -> None:
+        if self.handle:
+            h, self.handle = self.handle, None
+            _check(lib().sdm_icl_attn_release(h))
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.release()
+
+
+def sdm_icl_attn_fit(q, k, v, length: int, scale_mode: int = SDM_ICL_SCALE_NONE,
+                     precision: int = SDM_ICL_PREC_AUTO, head_coef=None, gate=None,
+                     out_ctx=None, stream=None) -> Cache:
+    """Build the K/V cache from context q/k/v ``[B, N_pad, H, 64]`` (fp16) with
+    ``length`` valid rows; if ``out_ctx`` (same shape) is given, the context
+    self-attention is written there too."""
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be [B, N_pad, H, D]")
+    B, N, H, D = q.shape
+    for name, t in (("k", k), ("v", v)):
+        if tuple(t.shape) != (B, N, H, D):
+            raise ValueError(f"{name} must have the shape of q")
+    if gate is not None and tuple(gate.shape) != (B, N, H):
+        raise ValueError("gate must be [B, N_pad, H]")
+    if out_ctx is not None and tuple(out_ctx.shape) != (B, N, H, D):
+        raise ValueError("out_ctx must have the shape of q")
+    lengths = (ctypes.c_int64 * B)(*([int(length)] * B))
+    coef = None
+    if head_coef is not None:
+        coef_np = np.ascontiguousarray(head_coef, dtype=np.float32)
+        coef = coef_np.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    f16 = torch.float16
+    args = FitArgs(batch=B, rows_padded=N, heads=H, head_dim=D, lengths=lengths,
+                   q=_dev_ptr(q, "q", f16), k=_dev_ptr(k, "k", f16), v=_dev_ptr(v, "v", f16),
+                   gate=_dev_ptr(gate, "gate", f16), head_coef=coef, scale_mode=scale_mode,
+                   precision=precision, out_ctx=_dev_ptr(out_ctx, "out_ctx", f16),
+                   stream=_stream_ptr(stream))
+    handle = ctypes.c_void_p()
+    _check(lib().sdm_icl_attn_fit(ctypes.byref(args), ctypes.byref(handle)))
+    return Cache(handle.value)
+
+
+def sdm_icl_attn_query_workspace_size(cache: Cache, n_query: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().sdm_icl_attn_query_workspace_size(cache.handle, int(n_query), ctypes.byref(b)))
+    return b.value
+
+
+def sdm_icl_attn_query(cache: Cache, q, gate=None, out=None, workspace=None, stream=None):
+    """Query rows q ``[B, R, H, 64]`` attend to the cache; returns ``out``."""
+    import torch
+    B, R, H, D = q.shape
+    if gate is not None and tuple(gate.shape) != (B, R, H):
+        raise ValueError("gate must be [B, R, H]")
+    if out is None:
+        out = torch.empty_like(q)
+    elif tuple(out.shape) != (B, R, H, D):
+        raise ValueError("out must have the shape of q")
+    need = sdm_icl_attn_query_workspace_size(cache, R)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().sdm_icl_attn_query(cache.handle, _dev_ptr(q, "q", torch.float16),
+                                    _dev_ptr(gate, "gate", torch.float16), R,
+                                    _dev_ptr(out, "out", torch.float16),
+                                    _dev_ptr(workspace, "workspace"), ws_bytes, _stream_ptr(stream)))
+    return out
+
+
+def sdm_icl_attn_cache_info(cache: Cache) -> dict:
+    info = CacheInfo()
+    _check(lib().sdm_icl_attn_cache_info(cache.handle, ctypes.byref(info)))
+    return {name: getattr(info, name) for name, _ in CacheInfo._fields_}
+
+
+def sdm_icl_attn_cache_export(cache: Cache, stream=None):
+    """(K ``[B,H,n,D]``, V ``[B,H,n,D]``, scales ``[3,B,H]``) on the host:
+    uint8 e4m3 codes in FP8 mode, float16 in FP16 mode."""
+    i = sdm_icl_attn_cache_info(cache)
+    dt = np.uint8 if i["precision"] == SDM_ICL_PREC_FP8_E4M3 else np.float16
+    shape = (i["batch"], i["heads"], i["n_valid"], i["head_dim"])
+    k = np.empty(shape, dtype=dt)
+    v = np.empty(shape, dtype=dt)
+    sc = np.empty((3, i["batch"], i["heads"]), dtype=np.float32)
+    _check(lib().sdm_icl_attn_cache_export(cache.handle, k.ctypes.data, v.ctypes.data,
+                                           sc.ctypes.data, _stream_ptr(stream)))
+    return k, v, sc
+
+
+def sdm_icl_attn_release(cache: Cache) -> None:
+    cache.release()
+
+
+def sdm_icl_log_scale(q, key_length: int, head_coef=None, scale_mode: int = SDM_ICL_SCALE_LOG,
+                      gate=None, q_inv_scale=None, out=None, stream=None):
+    """Fused shared-length scaling of q ``[B, rows, H, 64]``; returns the
+    head-major ``[B, H, rows, 64]`` fp16 rows, or e4m3 codes (uint8) when
+    ``q_inv_scale`` (device float32 ``[B, H]``) is given."""
+    import torch
+    B, R, H, D = q.shape
+    if out is None:
+        dtype = torch.uint8 if q_inv_scale is not None else torch.float16
+        out = torch.empty((B, H, R, D), dtype=dtype, device=q.device)
+    coef = None
+    if head_coef is not None:
+        coef_np = np.ascontiguousarray(head_coef, dtype=np.float32)
+        coef = coef_np.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    _check(lib().sdm_icl_log_scale(_dev_ptr(q, "q", torch.float16), _dev_ptr(gate, "gate", torch.float16),
+                                   B, R, H, D, int(key_length), coef, scale_mode,
+                                   _dev_ptr(q_inv_scale, "q_inv_scale", torch.float32),
+                                   _dev_ptr(out, "out"), _stream_ptr(stream)))
+    return out

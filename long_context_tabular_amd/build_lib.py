@@ -1,0 +1,63 @@
+"""Build the gfx950 shared library ``libsdm_icl_attn.so`` in-tree with hipcc.
+
+Every HIP source is compiled for gfx950 only, with packed-FP32 instruction
+selection disabled and FMA contraction off (the scaling and quantisation
+kernels must round exactly where the method rounds; the attention kernel
+writes its FMAs explicitly).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIB_NAME = "libsdm_icl_attn.so"
+LIB_PATH = os.path.join(PKG, LIB_NAME)
+SOURCES = ["prep.hip", "attention.hip", "sdm_icl_attn.cpp"]
+
+HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
+COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-ffp-contract=off",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass warns that it does not know the packed-fp32 feature: harmless
+    noise = "packed-fp32-ops"
+    err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build failed: {' '.join(cmd)}\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+
+
+def build(verbose: bool = False, save_temps_dir: str | None = None) -> str:
+    """Compile all sources and link the shared library; returns its path."""
+    with tempfile.TemporaryDirectory() as tmp:
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(tmp, src + ".o")
+            extra = []
+            if save_temps_dir and src.endswith(".hip"):
+                os.makedirs(save_temps_dir, exist_ok=True)
+                obj = os.path.join(save_temps_dir, src + ".o")
+                extra = ["-save-temps=obj"]
+            _run([HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+            objs.append(obj)
+        out_tmp = LIB_PATH + ".tmp"
+        _run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", out_tmp], verbose)
+        os.replace(out_tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv,
+                save_temps_dir=os.path.join(ROOT, "_build", "temps") if "--save-temps" in sys.argv else None))

@@ -1,0 +1,411 @@
+// Flash-style row-wise ICL attention on gfx950 (CDNA4), FP16 or FP8 e4m3.
+//
+//   K3  context self-attention: every valid context row attends to all n
+//       context keys, no causal mask; rows >= n are written as zeros.
+//   K4  cached query attention: the same tile loop over one KV split of the
+//       resident cache, writing (m, l, O) partials.
+//   K5  combine: one wavefront per (b, h, row), lane = head-dim element,
+//       merges the splits in a fixed order.
+//
+// Semantics: scaled dot-product attention of the (scaled, optionally
+// quantised) queries over the cached keys/values, as in "[FP8 3/4] Integrate
+// FP8 attention and caching into TabICLv2" (shared attention projects Q/K/V
+// and falls back to SDPA; FP8 Q/K/V with per-head scales).
+//
+// Data flow of one workgroup (4 wavefronts, each owning QG x 32 query rows):
+//   * Q stays in VGPRs for the whole KV loop (MFMA B operand).
+//   * 64-key tiles of K and of V are fetched as separate loads into registers
+//     one tile ahead, and written into separate double-buffered LDS stages
+//     (K row-major, V transposed and widened to fp16), one barrier per tile.
+//   * S^T = K Q^T with v_mfma_f32_32x32x64_f8f6f4 (FP8) or 32x32x16_f16.
+//     K rows are fed in a permuted order so that each lane ends up holding,
+//     for its own query, exactly the 8-key groups that the PV MFMA wants in
+//     its B operand: P never leaves registers.
+//   * Online softmax in base 2 (the scale is folded into one FMA per score),
+//     with a lazily moved reference maximum: O and l are rescaled only when a
+//     tile's maximum exceeds the reference by more than 8 (so p <= 256).
+//   * O^T += V^T P^T with v_mfma_f32_32x32x16_f16; P is rounded to fp16
+//     (nearest even) and l is summed from the same rounded P (v_dot2).
+// Every per-row quantity depends only on that row's own scores, so a row's
+// result is independent of the other rows in the launch.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace sdm {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __fp16 h16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr float kRescaleThreshold = 8.0f;  // log2 units: p <= 2^8 between rescales
+
+// Row r of a 32-row MFMA A operand holds key sigma(r) of its 32-key chunk:
+// bits 2 and 3 of r swapped.  With the 32x32 output layout (lane l, register
+// a holds row 8(a/4) + 4(l/32) + a%4), lane-half hf then holds keys
+// 8hf..8hf+7 in registers 0..7 and 16+8hf..16+8hf+7 in registers 8..15.
+__device__ constexpr int sigma(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+
+// Value of lane l and of lane l^32, returned in (low half, high half) order on
+// both halves so that both compute identical reductions.
+__device__ inline void halves(float x, float& lo, float& hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  lo = __uint_as_float(r[0]);
+  hi = __uint_as_float(r[1]);
+}
+
+template <int PREC>
+struct Ops;
+
+template <>
+struct Ops<kPrecFp8> {
+  static constexpr int EB = 1;          // bytes per cached element
+  static constexpr int KROW = 80;       // LDS bytes per K row (64 + 16 pad)
+  typedef i32x8 QFrag;                  // 32 e4m3 codes: d in [32hf, 32hf+32)
+  __device__ static QFrag load_q(const unsigned char* rowp, int hf) {
+    return *reinterpret_cast<const i32x8*>(rowp + 32 * hf);
+  }
+  __device__ static f32x16 qk(const unsigned char* krow, int hf, const QFrag& q) {
+    const i32x4 a0 = *reinterpret_cast<const i32x4*>(krow + 32 * hf);
+    const i32x4 a1 = *reinterpret_cast<const i32x4*>(krow + 32 * hf + 16);
+    const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    const f32x16 z = {};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, q, z, 0, 0, 0, 0, 0, 0);
+  }
+};
+
+template <>
+struct Ops<kPrecFp16> {
+  static constexpr int EB = 2;
+  static constexpr int KROW = 144;      // 128 + 16 pad
+  struct QFrag { f16x8 v[4]; };         // slice t: d in [16t + 8hf, +8)
+  __device__ static QFrag load_q(const unsigned char* rowp, int hf) {
+    QFrag f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) f.v[t] = *reinterpret_cast<const f16x8*>(rowp + 32 * t + 16 * hf);
+    return f;
+  }
+  __device__ static f32x16 qk(const unsigned char* krow, int hf, const QFrag& q) {
+    f32x16 acc = {};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const f16x8 a = *reinterpret_cast<const f16x8*>(krow + 32 * t + 16 * hf);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, q.v[t], acc, 0, 0, 0);
+    }
+    return acc;
+  }
+};
+
+constexpr int kVRow = 144;  // LDS bytes per d-row of the fp16 V^T tile (128 + 16 pad)
+
+// Staging registers of one thread for one K tile and one V tile: 16 d of one
+// key (K, row-major) and 16 keys of one d (V, tile-transposed).
+template <int EB>
+struct Stage { i32x4 k[EB]; i32x4 v[EB]; };
+
+template <int PREC, int QG, bool SPLIT>
+__global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
+  typedef Ops<PREC> O;
+  constexpr int EB = O::EB;
+  constexpr int QT = kWaves * QG * 32;
+  constexpr int KTILE = 64 * O::KROW;
+  constexpr int VTILE = 64 * kVRow;
+  __shared__ __attribute__((aligned(16))) unsigned char kbuf[2][KTILE];
+  __shared__ __attribute__((aligned(16))) unsigned char vbuf[2][VTILE];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 31, hf = lane >> 5;
+  const int bh = blockIdx.z;
+  const int b = bh / a.heads, h = bh - b * a.heads;
+  const int64_t q0 = (int64_t)blockIdx.x * QT;
+  const int split = blockIdx.y;
+
+  if (q0 >= a.q_rows_valid) {
+    if constexpr (!SPLIT) {
+      // rows past the valid context: zeros (16 bytes per thread per step)
+      const int64_t r_end = a.out_rows < q0 + QT ? a.out_rows : q0 + QT;
+      for (int64_t i = tid; i < (r_end - q0) * 8; i += kThreads) {
+        const int64_t r = q0 + i / 8;
+        reinterpret_cast<i32x4*>(a.out)[((int64_t)b * a.out_rows + r) * a.heads * 8 + h * 8 + (i & 7)] =
+            i32x4{0, 0, 0, 0};
+      }
+    }
+    return;
+  }
+
+  float c_scale = a.tau_log2e;  // logit (log2 units) = raw dot * c_scale
+  float sv = 1.0f;
+  if constexpr (PREC == kPrecFp8) {
+    c_scale *= a.scales[bh] * a.scales[a.bh_count + bh];
+    sv = a.scales[2 * a.bh_count + bh];
+  }
+
+  // Q fragments for this wave's QG x 32 rows
+  const unsigned char* qbase = reinterpret_cast<const unsigned char*>(a.q);
+  typename O::QFrag qf[QG];
+  const int64_t wq0 = q0 + (int64_t)w * QG * 32;
+#pragma unroll
+  for (int g = 0; g < QG; ++g)
+    qf[g] = O::load_q(qbase + (((int64_t)bh * a.q_rows_alloc) + wq0 + g * 32 + col) * 64 * EB, hf);
+
+  const int64_t n_tiles = a.n_alloc / 64;
+  const int64_t t0 = (int64_t)split * a.tiles_per_split;
+  const int64_t t1 = n_tiles < t0 + a.tiles_per_split ? n_tiles : t0 + a.tiles_per_split;
+
+  const unsigned char* kg = reinterpret_cast<const unsigned char*>(a.kc) + (int64_t)bh * a.n_alloc * 64 * EB;
+  const unsigned char* vg = reinterpret_cast<const unsigned char*>(a.vt) + (int64_t)bh * a.n_alloc * 64 * EB;
+
+  // thread -> staging coordinates: K key kr = tid/4, d-quarter tid%4;
+  //                                 V d-row tid/4, key-quarter tid%4
+  const int sr = tid >> 2, sq = tid & 3;
+  const int k_lds = (32 * (sr >> 5) + sigma(sr & 31)) * O::KROW + sq * 16 * EB;
+  const int v_lds = sr * kVRow + sq * 32;
+
+  auto load_stage = [&](int64_t t, Stage<EB>& st) {
+    const i32x4* kp = reinterpret_cast<const i32x4*>(kg + t * 64 * 64 * EB + tid * 16 * EB);
+    const i32x4* vp = reinterpret_cast<const i32x4*>(vg + t * 64 * 64 * EB + tid * 16 * EB);
+#pragma unroll
+    for (int c = 0; c < EB; ++c) st.k[c] = kp[c];
+#pragma unroll
+    for (int c = 0; c < EB; ++c) st.v[c] = vp[c];
+  };
+  auto store_stage = [&](int buf, const Stage<EB>& st) {
+#pragma unroll
+    for (int c = 0; c < EB; ++c) *reinterpret_cast<i32x4*>(&kbuf[buf][k_lds + 16 * c]) = st.k[c];
+    if constexpr (PREC == kPrecFp8) {
+      // widen 16 e4m3 codes to fp16 (exact) once per workgroup
+      i32x4 lo, hi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int word = st.v[0][e];
+        const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, false);
+        const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, true);
+        const int w0 = __builtin_bit_cast(int, p0), w1 = __builtin_bit_cast(int, p1);
+        if (e < 2) { lo[2 * e] = w0; lo[2 * e + 1] = w1; }
+        else { hi[2 * (e - 2)] = w0; hi[2 * (e - 2) + 1] = w1; }
+      }
+      *reinterpret_cast<i32x4*>(&vbuf[buf][v_lds]) = lo;
+      *reinterpret_cast<i32x4*>(&vbuf[buf][v_lds + 16]) = hi;
+    } else {
+      *reinterpret_cast<i32x4*>(&vbuf[buf][v_lds]) = st.v[0];
+      *reinterpret_cast<i32x4*>(&vbuf[buf][v_lds + 16]) = st.v[1];
+    }
+  };
+
+  float m_run[QG], l_run[QG];
+  f32x16 o[QG][2];
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
+    m_run[g] = -INFINITY;
+    l_run[g] = 0.f;
+    o[g][0] = f32x16{};
+    o[g][1] = f32x16{};
+  }
+
+  Stage<EB> st;
+  load_stage(t0, st);
+  store_stage(0, st);
+  if (t0 + 1 < t1) load_stage(t0 + 1, st);
+  __syncthreads();
+
+  const h16x2 ones = {(__fp16)1.0f, (__fp16)1.0f};
+
+  for (int64_t t = t0; t < t1; ++t) {
+    const int cur = (int)((t - t0) & 1);
+    const unsigned char* kb = kbuf[cur];
+    const unsigned char* vb = vbuf[cur];
+
+    // ---- S^T = K Q^T, two 32-key chunks
+    f32x16 s[QG][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int g = 0; g < QG; ++g) s[g][c] = O::qk(kb + (32 * c + col) * O::KROW, hf, qf[g]);
+    }
+
+    // ---- online softmax (base 2)
+    const bool last = (t + 1) * 64 > a.n;
+    f16x8 p16[QG][2][2];
+#pragma unroll
+    for (int g = 0; g < QG; ++g) {
+      if (last) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t key = t * 64 + 32 * c + 16 * (r >> 3) + 8 * hf + (r & 7);
+            if (key >= a.n) s[g][c][r] = -INFINITY;
+          }
+      }
+      float mx = s[g][0][0];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[g][c][r]);
+      float lo, hi;
+      halves(mx, lo, hi);
+      const float mcand = fmaxf(lo, hi) * c_scale;
+      const bool move = mcand > m_run[g] + kRescaleThreshold;
+      if (__builtin_amdgcn_ballot_w64(move) != 0) {  // wave-uniform branch
+        const float mnew = move ? mcand : m_run[g];
+        const float alpha = __builtin_amdgcn_exp2f(m_run[g] - mnew);  // exactly 1 when unmoved
+        m_run[g] = mnew;
+        l_run[g] *= alpha;
+        o[g][0] *= alpha;
+        o[g][1] *= alpha;
+      }
+      const float neg_m = -m_run[g];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            p16[g][c][ks][e] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[g][c][8 * ks + e], c_scale, neg_m));
+      // l from the same rounded P: each packed 32-bit word of P is one
+      // fp16 pair, summed into fp32 by v_dot2 with (1, 1)
+      float lsum = l_run[g];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const f16x8 pv = p16[g][c][ks];
+          const i32x4 words = __builtin_bit_cast(i32x4, pv);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // copy the element first: bit-casting a vector element directly
+            // reads element 0 with this compiler
+            const int word = words[i];
+            lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, word), ones, lsum, false);
+          }
+        }
+      l_run[g] = lsum;
+    }
+
+    // ---- O^T += V^T P^T
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+          const f16x8 va = *reinterpret_cast<const f16x8*>(vb + (32 * dt + col) * kVRow +
+                                                           (32 * c + 16 * ks + 8 * hf) * 2);
+#pragma unroll
+          for (int g = 0; g < QG; ++g)
+            o[g][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, p16[g][c][ks], o[g][dt], 0, 0, 0);
+        }
+
+    // ---- stage the next tile (its loads were issued one iteration ago)
+    if (t + 1 < t1) {
+      store_stage(cur ^ 1, st);
+      if (t + 2 < t1) load_stage(t + 2, st);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
+    float lo, hi;
+    halves(l_run[g], lo, hi);
+    const float l_tot = lo + hi;
+    const int64_t q = wq0 + g * 32 + col;
+    if constexpr (SPLIT) {
+      if (q < a.q_rows_valid) {
+        const int64_t slot = ((int64_t)bh * a.q_rows_valid + q) * a.splits + split;
+        if (hf == 0) *reinterpret_cast<float2*>(a.part_ml + slot * 2) = float2{m_run[g], l_tot};
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const f32x4 v4 = {o[g][dt][4 * p], o[g][dt][4 * p + 1], o[g][dt][4 * p + 2], o[g][dt][4 * p + 3]};
+            *reinterpret_cast<f32x4*>(a.part_o + slot * 64 + 32 * dt + 8 * p + 4 * hf) = v4;
+          }
+      }
+    } else {
+      if (q < a.out_rows) {
+        const bool valid = q < a.q_rows_valid;
+        const float f = valid ? sv / l_tot : 0.f;
+        uint16_t* orow = a.out + (((int64_t)b * a.out_rows + q) * a.heads + h) * 64;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            f16x4 v4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v4[e] = valid ? (_Float16)(o[g][dt][4 * p + e] * f) : (_Float16)0.0f;
+            *reinterpret_cast<f16x4*>(orow + 32 * dt + 8 * p + 4 * hf) = v4;
+          }
+      }
+    }
+  }
+}
+
+// One wavefront per (b, h, row); lane = head-dim element.  Fixed split order.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_o,
+                                                      const float* __restrict__ part_ml,
+                                                      const float* __restrict__ s_v, int B, int H,
+                                                      int64_t rows, int splits, int fp8,
+                                                      uint16_t* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b*H + h) * rows + r
+  if (item >= (int64_t)B * H * rows) return;
+  const int64_t bh = item / rows, r = item - bh * rows;
+  const int b = (int)(bh / H), h = (int)(bh - (int64_t)b * H);
+  const float* ml = part_ml + item * splits * 2;
+  const float* po = part_o + item * splits * 64;
+  float m = -INFINITY;
+  for (int s = 0; s < splits; ++s) m = fmaxf(m, ml[2 * s]);
+  float l = 0.f, acc = 0.f;
+  for (int s = 0; s < splits; ++s) {
+    const float wgt = __builtin_amdgcn_exp2f(ml[2 * s] - m);
+    l = __builtin_fmaf(wgt, ml[2 * s + 1], l);
+    acc = __builtin_fmaf(wgt, po[s * 64 + lane], acc);
+  }
+  const float sv = fp8 ? s_v[bh] : 1.0f;
+  const _Float16 y = (_Float16)(acc * (sv / l));
+  out[((int64_t)b * rows + r) * H * 64 + h * 64 + lane] = __builtin_bit_cast(uint16_t, y);
+}
+
+}  // namespace
+
+hipError_t launch_attention(const AttnArgs& a, int prec, bool split, hipStream_t s) {
+  // FP8: wide query tiles (2 x 32 rows per wave) when there are many rows.
+  // FP16 keeps one 32-row group per wave (its Q fragment is twice as large).
+  const bool wide = prec == kPrecFp8 && a.q_rows_valid > 128;
+  const int qt = kWaves * 32 * (wide ? 2 : 1);
+  const int64_t rows = split ? a.q_rows_valid : a.out_rows;
+  const dim3 grid((unsigned)((rows + qt - 1) / qt), (unsigned)a.splits, (unsigned)a.bh_count);
+#define SDM_ATT(P, G, S) hipLaunchKernelGGL((attention_kernel<P, G, S>), grid, dim3(kThreads), 0, s, a)
+  if (prec == kPrecFp8) {
+    if (wide) { if (split) SDM_ATT(kPrecFp8, 2, true); else SDM_ATT(kPrecFp8, 2, false); }
+    else { if (split) SDM_ATT(kPrecFp8, 1, true); else SDM_ATT(kPrecFp8, 1, false); }
+  } else {
+    if (wide) { if (split) SDM_ATT(kPrecFp16, 2, true); else SDM_ATT(kPrecFp16, 2, false); }
+    else { if (split) SDM_ATT(kPrecFp16, 1, true); else SDM_ATT(kPrecFp16, 1, false); }
+  }
+#undef SDM_ATT
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const float* part_o, const float* part_ml, const float* s_v, int B,
+                          int H, int64_t rows, int splits, int prec, uint16_t* out,
+                          hipStream_t s) {
+  const int64_t items = (int64_t)B * H * rows;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, part_o,
+                     part_ml, s_v, B, H, rows, splits, prec == kPrecFp8 ? 1 : 0, out);
+  return hipGetLastError();
+}
+
+}  // namespace sdm

@@ -1,0 +1,521 @@
+// Host layer of the C ABI declared in include/sdm_icl_attn.h: argument
+// validation, the shared-length scalar preparation, the KV split plan, cache
+// handle lifetime and the launch sequences of fit and query.
+//
+// fit   = [FP8: amax -> scales] -> pack K/V -> [out_ctx: scale Q -> attention]
+// query = scale (+quantise) queries -> split-KV attention -> combine
+// Everything is enqueued on the caller's stream; nothing synchronises the host
+// except cache_export.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <unordered_set>
+#include <vector>
+
+#include "../../include/sdm_icl_attn.h"
+#include "internal.h"
+
+using namespace sdm;
+
+struct sdm_icl_cache_s {
+  uint64_t magic;
+  int device;
+  hipStream_t stream;
+  int32_t B, H, D, prec, mode, splits;
+  int64_t n, n_alloc, tiles_per_split;
+  float L32;
+  HeadFactors kh;
+  void* block;     // one device allocation: [kc][vt][scales 3BH][inv 3BH]
+  void* kc;
+  void* vt;
+  float* scales;
+  float* inv;
+  size_t bytes;
+};
+
+namespace {
+
+constexpr uint64_t kMagic = 0x5344'4D49'434C'4131ull;  // "SDMICLA1"
+constexpr int64_t kFp8MinRows = 8192;
+constexpr int kTargetSplitsPerCu = 4;  // splits = num_cus / 4 (64 on 256 CUs)
+constexpr int64_t kMinTilesPerSplit = 4;
+
+thread_local std::string g_error;
+
+std::mutex g_registry_mu;
+std::unordered_set<const sdm_icl_cache_s*> g_registry;
+
+sdm_icl_status fail(sdm_icl_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+sdm_icl_status hip_fail(hipError_t e, const char* what) {
+  (void)hipGetLastError();
+  return fail(e == hipErrorOutOfMemory ? SDM_ICL_E_OOM : SDM_ICL_E_HIP, "%s: %s", what,
+              hipGetErrorString(e));
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// fp32 -> fp16 bits, round to nearest even (host side of the head factors).
+// The fp16 grid spacing in the binade of f is 2^(max(E,-14)-10); the 24-bit
+// significand is shifted down to that spacing and rounded half to even.
+uint16_t f32_to_f16_bits(float f) {
+  uint32_t x;
+  std::memcpy(&x, &f, 4);
+  const uint16_t sign = (uint16_t)((x >> 16) & 0x8000u);
+  const uint32_t ax = x & 0x7FFFFFFFu;
+  if (ax > 0x7F800000u) return (uint16_t)(sign | 0x7E00u);  // NaN
+  if (ax >= 0x47800000u) return (uint16_t)(sign | 0x7C00u); // |f| >= 65536: inf
+  if (ax <= 0x33000000u) return sign;                       // |f| <= 2^-25: zero
+  const int E = (int)(ax >> 23) - 127;
+  const uint32_t M = (ax & 0x7FFFFFu) | 0x800000u;
+  const int sh = 13 + (E < -14 ? -14 - E : 0);               // 13..24
+  uint32_t q = M >> sh;
+  const uint32_t rem = M & ((1u << sh) - 1u), half = 1u << (sh - 1);
+  if (rem > half || (rem == half && (q & 1u))) ++q;
+  uint32_t h = E < -14 ? q : ((uint32_t)(E + 14) << 10) + q; // a carry moves the exponent
+  if (h > 0x7C00u) h = 0x7C00u;
+  return (uint16_t)(sign | h);
+}
+
+float length_scalar(int64_t n) { return (float)std::log((double)(n > 1 ? n : 1)); }
+
+void head_factors(int64_t n, const float* coef, int H, HeadFactors* out) {
+  const float L = length_scalar(n);
+  for (int h = 0; h < kMaxHeads; ++h)
+    out->bits[h] = h < H ? f32_to_f16_bits(L * coef[h]) : (uint16_t)0;
+}
+
+int32_t resolve_precision(int64_t n, int32_t requested) {
+  if (requested == SDM_ICL_PREC_AUTO) return n > kFp8MinRows ? SDM_ICL_PREC_FP8_E4M3 : SDM_ICL_PREC_FP16;
+  return requested;
+}
+
+void plan_splits(int64_t n, int32_t num_cus, int32_t* splits, int64_t* tiles_per_split) {
+  const int64_t tiles = (n + kKeyTile - 1) / kKeyTile;
+  int64_t target = num_cus / kTargetSplitsPerCu;
+  if (target < 1) target = 1;
+  int64_t tps = (tiles + target - 1) / target;
+  if (tps < kMinTilesPerSplit) tps = kMinTilesPerSplit;
+  if (tps > tiles) tps = tiles;
+  *tiles_per_split = tps;
+  *splits = (int32_t)((tiles + tps - 1) / tps);
+}
+
+struct DeviceInfo {
+  bool known = false, gfx950 = false;
+  int cus = 0;
+};
+std::mutex g_dev_mu;
+DeviceInfo g_dev[64];
+
+sdm_icl_status current_device(int* dev, DeviceInfo* info) {
+  hipError_t e = hipGetDevice(dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (*dev < 0 || *dev >= 64) return fail(SDM_ICL_E_DEVICE, "device ordinal %d out of range", *dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DeviceInfo& d = g_dev[*dev];
+  if (!d.known) {
+    hipDeviceProp_t p;
+    e = hipGetDeviceProperties(&p, *dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    d.gfx950 = std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+    d.cus = p.multiProcessorCount;
+    d.known = true;
+  }
+  *info = d;
+  if (!d.gfx950) return fail(SDM_ICL_E_DEVICE, "device %d is not gfx950", *dev);
+  return SDM_ICL_OK;
+}
+
+sdm_icl_status check_device_ptr(const void* p, int dev, const char* name) {
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, p);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(SDM_ICL_E_DEVICE, "%s is not HIP device memory", name);
+  }
+  if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeManaged)
+    return fail(SDM_ICL_E_DEVICE, "%s is not device memory", name);
+  if (attr.device != dev)
+    return fail(SDM_ICL_E_DEVICE, "%s is on device %d, the stream's device is %d", name, attr.device, dev);
+  return SDM_ICL_OK;
+}
+
+bool live(const sdm_icl_cache_s* c) {
+  std::lock_guard<std::mutex> lk(g_registry_mu);
+  return c != nullptr && g_registry.count(c) != 0 && c->magic == kMagic;
+}
+
+struct QueryLayout {
+  size_t q_off, po_off, ml_off, total;
+  int64_t q_rows_alloc;
+};
+
+QueryLayout query_layout(const sdm_icl_cache_s* c, int64_t R) {
+  QueryLayout L;
+  const int64_t eb = c->prec == SDM_ICL_PREC_FP8_E4M3 ? 1 : 2;
+  L.q_rows_alloc = round_up(R, kQueryPad);
+  L.q_off = 0;
+  size_t off = (size_t)round_up((int64_t)c->B * c->H * L.q_rows_alloc * kHeadDim * eb, 256);
+  L.po_off = off;
+  if (c->splits > 1) {
+    off += (size_t)round_up((int64_t)c->B * c->H * R * c->splits * kHeadDim * 4, 256);
+    L.ml_off = off;
+    off += (size_t)round_up((int64_t)c->B * c->H * R * c->splits * 2 * 4, 256);
+  } else {
+    L.ml_off = off;
+  }
+  L.total = off;
+  return L;
+}
+
+AttnArgs attn_args(const sdm_icl_cache_s* c) {
+  AttnArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.kc = c->kc;
+  a.vt = c->vt;
+  a.scales = c->scales;
+  a.n = c->n;
+  a.n_alloc = c->n_alloc;
+  a.heads = c->H;
+  a.bh_count = c->B * c->H;
+  a.tau_log2e = (float)(1.4426950408889634 / std::sqrt((double)kHeadDim));
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t sdm_icl_version(void) { return 100; }
+
+const char* sdm_icl_last_error(void) { return g_error.c_str(); }
+
+float sdm_icl_length_scalar(int64_t n) { return length_scalar(n); }
+
+sdm_icl_status sdm_icl_head_factors(int64_t n, const float* head_coef, int32_t heads,
+                                    uint16_t* out_fp16_bits) {
+  if (!head_coef || !out_fp16_bits) return fail(SDM_ICL_E_INVALID, "head_factors: null pointer");
+  if (heads < 1 || heads > kMaxHeads) return fail(SDM_ICL_E_INVALID, "heads must be in 1..%d", kMaxHeads);
+  HeadFactors kh;
+  head_factors(n, head_coef, heads, &kh);
+  std::memcpy(out_fp16_bits, kh.bits, sizeof(uint16_t) * heads);
+  return SDM_ICL_OK;
+}
+
+int32_t sdm_icl_select_precision(int64_t n, int32_t requested) { return resolve_precision(n, requested); }
+
+sdm_icl_status sdm_icl_split_plan(int64_t n, int32_t num_cus, int32_t* kv_splits,
+                                  int64_t* keys_per_split) {
+  if (!kv_splits || !keys_per_split) return fail(SDM_ICL_E_INVALID, "split_plan: null pointer");
+  if (n < 1 || num_cus < 1) return fail(SDM_ICL_E_INVALID, "split_plan: need n >= 1 and num_cus >= 1");
+  int64_t tps;
+  plan_splits(n, num_cus, kv_splits, &tps);
+  *keys_per_split = tps * kKeyTile;
+  return SDM_ICL_OK;
+}
+
+sdm_icl_status sdm_icl_attn_fit(const sdm_icl_fit_args* a, sdm_icl_cache* out) {
+  // ---- host-side validation (nothing touches the device before this passes)
+  if (!a || !out) return fail(SDM_ICL_E_INVALID, "fit: null args or out");
+  if (a->batch < 1 || a->rows_padded < 1 || a->heads < 1)
+    return fail(SDM_ICL_E_INVALID, "fit: batch, rows_padded and heads must be >= 1");
+  if (a->heads > kMaxHeads) return fail(SDM_ICL_E_UNSUPPORTED, "fit: at most %d heads", kMaxHeads);
+  if (a->head_dim != kHeadDim) return fail(SDM_ICL_E_UNSUPPORTED, "fit: head_dim must be 64 (got %d)", a->head_dim);
+  if (!a->lengths) return fail(SDM_ICL_E_INVALID, "fit: lengths is NULL");
+  const int64_t n = a->lengths[0];
+  for (int b = 1; b < a->batch; ++b)
+    if (a->lengths[b] != n)
+      return fail(SDM_ICL_E_UNSUPPORTED, "fit: per-batch lengths differ (only a shared length is supported)");
+  if (n < 1 || n > a->rows_padded) return fail(SDM_ICL_E_INVALID, "fit: need 1 <= n <= rows_padded (n=%lld)", (long long)n);
+  if (!a->q || !a->k || !a->v) return fail(SDM_ICL_E_INVALID, "fit: q, k and v are required");
+  if (a->scale_mode < SDM_ICL_SCALE_NONE || a->scale_mode > SDM_ICL_SCALE_GATED_LOG)
+    return fail(SDM_ICL_E_INVALID, "fit: unknown scale_mode %d", a->scale_mode);
+  if ((a->gate != nullptr) != (a->scale_mode == SDM_ICL_SCALE_GATED_LOG))
+    return fail(SDM_ICL_E_INVALID, "fit: gate must be given exactly when scale_mode is GATED_LOG");
+  if ((a->head_coef != nullptr) != (a->scale_mode != SDM_ICL_SCALE_NONE))
+    return fail(SDM_ICL_E_INVALID, "fit: head_coef must be given exactly when scale_mode is LOG or GATED_LOG");
+  if (a->precision < SDM_ICL_PREC_FP16 || a->precision > SDM_ICL_PREC_AUTO)
+    return fail(SDM_ICL_E_INVALID, "fit: unknown precision %d", a->precision);
+  if ((int64_t)a->batch * a->rows_padded * a->heads > (int64_t)1 << 40)
+    return fail(SDM_ICL_E_INVALID, "fit: problem too large");
+
+  // ---- device checks
+  int dev;
+  DeviceInfo di;
+  sdm_icl_status st = current_device(&dev, &di);
+  if (st) return st;
+  const void* ptrs[] = {a->q, a->k, a->v, a->gate, a->out_ctx};
+  const char* names[] = {"q", "k", "v", "gate", "out_ctx"};
+  for (int i = 0; i < 5; ++i)
+    if (ptrs[i] && (st = check_device_ptr(ptrs[i], dev, names[i]))) return st;
+
+  hipStream_t s = (hipStream_t)a->stream;
+  const int B = a->batch, H = a->heads;
+  const int prec = resolve_precision(n, a->precision);
+  const int64_t eb = prec == SDM_ICL_PREC_FP8_E4M3 ? 1 : 2;
+  auto* c = new sdm_icl_cache_s();
+  c->magic = kMagic;
+  c->device = dev;
+  c->stream = s;
+  c->B = B; c->H = H; c->D = kHeadDim;
+  c->prec = prec;
+  c->mode = a->scale_mode;
+  c->n = n;
+  c->n_alloc = round_up(n, kKeyTile);
+  c->L32 = length_scalar(n);
+  if (a->scale_mode != SDM_ICL_SCALE_NONE) head_factors(n, a->head_coef, H, &c->kh);
+  else std::memset(&c->kh, 0, sizeof c->kh);
+  plan_splits(n, di.cus, &c->splits, &c->tiles_per_split);
+
+  const size_t kv_bytes = (size_t)B * H * c->n_alloc * kHeadDim * eb;
+  const size_t sc_bytes = (size_t)6 * B * H * sizeof(float);
+  c->bytes = 2 * kv_bytes + sc_bytes;
+  hipError_t e = hipMallocAsync(&c->block, c->bytes, s);
+  if (e != hipSuccess) { delete c; return hip_fail(e, "fit: cache allocation"); }
+  c->kc = c->block;
+  c->vt = (char*)c->block + kv_bytes;
+  c->scales = (float*)((char*)c->block + 2 * kv_bytes);
+  c->inv = c->scales + 3 * B * H;
+
+  // temporaries: amax scratch and the context Q operand
+  const int64_t q_rows_alloc = round_up(n, kQueryPad);
+  const size_t amax_bytes = (size_t)round_up(3 * B * H * 4, 256);
+  const size_t qctx_bytes = a->out_ctx ? (size_t)B * H * q_rows_alloc * kHeadDim * eb : 0;
+  void* tmp = nullptr;
+  if (amax_bytes + qctx_bytes) {
+    e = hipMallocAsync(&tmp, amax_bytes + qctx_bytes, s);
+    if (e != hipSuccess) {
+      (void)hipFreeAsync(c->block, s);
+      delete c;
+      return hip_fail(e, "fit: temporary allocation");
+    }
+  }
+  uint32_t* amax = (uint32_t*)tmp;
+  void* qctx = (char*)tmp + amax_bytes;
+  auto q16 = (const uint16_t*)a->q;
+  auto k16 = (const uint16_t*)a->k;
+  auto v16 = (const uint16_t*)a->v;
+  auto g16 = (const uint16_t*)a->gate;
+
+  if (prec == SDM_ICL_PREC_FP8_E4M3) {
+    e = launch_fp8_scales(q16, k16, v16, g16, B, a->rows_padded, n, H, a->scale_mode, c->kh, amax,
+                          c->scales, c->inv, s);
+  } else {
+    e = launch_fill_f32(c->scales, 6 * (int64_t)B * H, 1.0f, s);
+  }
+  if (e == hipSuccess)
+    e = launch_pack_kv(k16, v16, B, a->rows_padded, n, c->n_alloc, H, prec, c->inv + B * H,
+                       c->inv + 2 * B * H, c->kc, c->vt, s);
+  if (e == hipSuccess && a->out_ctx) {
+    e = launch_scale_queries(q16, g16, B, a->rows_padded, n, q_rows_alloc, H, a->scale_mode, c->kh,
+                             prec == SDM_ICL_PREC_FP8_E4M3 ? c->inv : nullptr, qctx, s);
+    if (e == hipSuccess) {
+      AttnArgs at = attn_args(c);
+      at.q = qctx;
+      at.q_rows_alloc = q_rows_alloc;
+      at.q_rows_valid = n;
+      at.out_rows = a->rows_padded;
+      at.out = (uint16_t*)a->out_ctx;
+      at.splits = 1;
+      at.tiles_per_split = (int32_t)(c->n_alloc / kKeyTile);
+      e = launch_attention(at, prec, false, s);
+    }
+  }
+  if (tmp) {
+    hipError_t e2 = hipFreeAsync(tmp, s);
+    if (e == hipSuccess) e = e2;
+  }
+  if (e != hipSuccess) {
+    (void)hipFreeAsync(c->block, s);
+    delete c;
+    return hip_fail(e, "fit: launch");
+  }
+  {
+    std::lock_guard<std::mutex> lk(g_registry_mu);
+    g_registry.insert(c);
+  }
+  *out = c;
+  return SDM_ICL_OK;
+}
+
+sdm_icl_status sdm_icl_attn_query_workspace_size(sdm_icl_cache c, int64_t n_query, size_t* bytes) {
+  if (!bytes) return fail(SDM_ICL_E_INVALID, "workspace_size: bytes is NULL");
+  if (!live(c)) return fail(SDM_ICL_E_STATE, "workspace_size: unknown or released cache");
+  if (n_query < 0) return fail(SDM_ICL_E_INVALID, "workspace_size: n_query < 0");
+  *bytes = query_layout(c, n_query).total;
+  return SDM_ICL_OK;
+}
+
+sdm_icl_status sdm_icl_attn_query(sdm_icl_cache c, const void* q, const void* gate, int64_t R,
+                                  void* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!live(c)) return fail(SDM_ICL_E_STATE, "query: unknown or released cache");
+  if (R < 0) return fail(SDM_ICL_E_INVALID, "query: n_query < 0");
+  if ((gate != nullptr) != (c->mode == SDM_ICL_SCALE_GATED_LOG))
+    return fail(SDM_ICL_E_INVALID, c->mode == SDM_ICL_SCALE_GATED_LOG
+                                       ? "query: the cache was fitted with GATED_LOG; a gate is required"
+                                       : "query: the cache was not fitted with GATED_LOG; gate must be NULL");
+  if (R == 0) return SDM_ICL_OK;
+  if (!q || !out || !ws) return fail(SDM_ICL_E_INVALID, "query: q, out and workspace are required");
+  if ((int64_t)c->B * R * c->H > (int64_t)1 << 40) return fail(SDM_ICL_E_INVALID, "query: too many rows");
+  const QueryLayout L = query_layout(c, R);
+  if (ws_bytes < L.total)
+    return fail(SDM_ICL_E_STATE, "query: workspace of %zu bytes is smaller than the %zu needed", ws_bytes, L.total);
+  int dev;
+  DeviceInfo di;
+  sdm_icl_status st = current_device(&dev, &di);
+  if (st) return st;
+  if (dev != c->device) return fail(SDM_ICL_E_DEVICE, "query: cache lives on device %d, current is %d", c->device, dev);
+  const void* ptrs[] = {q, gate, out, ws};
+  const char* names[] = {"q", "gate", "out", "workspace"};
+  for (int i = 0; i < 4; ++i)
+    if (ptrs[i] && (st = check_device_ptr(ptrs[i], dev, names[i]))) return st;
+
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  void* qbuf = w + L.q_off;
+  hipError_t e = launch_scale_queries((const uint16_t*)q, (const uint16_t*)gate, c->B, R, R, L.q_rows_alloc,
+                                      c->H, c->mode, c->kh,
+                                      c->prec == SDM_ICL_PREC_FP8_E4M3 ? c->inv : nullptr, qbuf, s);
+  if (e != hipSuccess) return hip_fail(e, "query: scale launch");
+  AttnArgs at = attn_args(c);
+  at.q = qbuf;
+  at.q_rows_alloc = L.q_rows_alloc;
+  at.q_rows_valid = R;
+  at.out_rows = R;
+  at.splits = c->splits;
+  at.tiles_per_split = (int32_t)c->tiles_per_split;
+  if (c->splits > 1) {
+    at.part_o = (float*)(w + L.po_off);
+    at.part_ml = (float*)(w + L.ml_off);
+    e = launch_attention(at, c->prec, true, s);
+    if (e == hipSuccess)
+      e = launch_combine(at.part_o, at.part_ml, c->scales + 2 * c->B * c->H, c->B, c->H, R, c->splits,
+                         c->prec, (uint16_t*)out, s);
+  } else {
+    at.out = (uint16_t*)out;
+    e = launch_attention(at, c->prec, false, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "query: attention launch");
+  return SDM_ICL_OK;
+}
+
+sdm_icl_status sdm_icl_attn_cache_info(sdm_icl_cache c, sdm_icl_cache_info* info) {
+  if (!info) return fail(SDM_ICL_E_INVALID, "cache_info: info is NULL");
+  if (!live(c)) return fail(SDM_ICL_E_STATE, "cache_info: unknown or released cache");
+  info->batch = c->B;
+  info->heads = c->H;
+  info->head_dim = c->D;
+  info->precision = c->prec;
+  info->scale_mode = c->mode;
+  info->kv_splits = c->splits;
+  info->n_valid = c->n;
+  info->rows_alloc = c->n_alloc;
+  info->keys_per_split = c->tiles_per_split * kKeyTile;
+  info->length_scalar = c->L32;
+  info->device_bytes = c->bytes;
+  return SDM_ICL_OK;
+}
+
+sdm_icl_status sdm_icl_attn_cache_export(sdm_icl_cache c, void* host_k, void* host_v,
+                                         float* host_scales, void* stream) {
+  if (!live(c)) return fail(SDM_ICL_E_STATE, "cache_export: unknown or released cache");
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t eb = c->prec == SDM_ICL_PREC_FP8_E4M3 ? 1 : 2;
+  const int64_t BH = (int64_t)c->B * c->H, row_bytes = kHeadDim * eb;
+  const size_t kv_bytes = (size_t)BH * c->n_alloc * row_bytes;
+  std::vector<unsigned char> tmp;
+  hipError_t e = hipSuccess;
+  if (host_k || host_v) tmp.resize(kv_bytes);
+  if (host_k) {
+    e = hipMemcpyAsync(tmp.data(), c->kc, kv_bytes, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "cache_export: K copy");
+    for (int64_t bh = 0; bh < BH; ++bh)
+      std::memcpy((char*)host_k + bh * c->n * row_bytes, tmp.data() + bh * c->n_alloc * row_bytes,
+                  (size_t)(c->n * row_bytes));
+  }
+  if (host_v) {
+    e = hipMemcpyAsync(tmp.data(), c->vt, kv_bytes, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "cache_export: V copy");
+    // tiles of [64 d][64 keys] -> rows [n][64 d]
+    const int64_t tiles = c->n_alloc / kKeyTile;
+    for (int64_t bh = 0; bh < BH; ++bh)
+      for (int64_t t = 0; t < tiles; ++t)
+        for (int d = 0; d < kHeadDim; ++d)
+          for (int j = 0; j < kKeyTile; ++j) {
+            const int64_t key = t * kKeyTile + j;
+            if (key >= c->n) break;
+            std::memcpy((char*)host_v + ((bh * c->n + key) * kHeadDim + d) * eb,
+                        tmp.data() + (((bh * tiles + t) * kHeadDim + d) * kKeyTile + j) * eb, (size_t)eb);
+          }
+  }
+  if (host_scales) {
+    e = hipMemcpyAsync(host_scales, c->scales, (size_t)3 * BH * sizeof(float), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "cache_export: scales copy");
+  }
+  return SDM_ICL_OK;
+}
+
+sdm_icl_status sdm_icl_attn_release(sdm_icl_cache c) {
+  {
+    std::lock_guard<std::mutex> lk(g_registry_mu);
+    if (!c || !g_registry.count(c)) return fail(SDM_ICL_E_STATE, "release: unknown or already released cache");
+    g_registry.erase(c);
+  }
+  c->magic = 0;
+  hipError_t e = hipFreeAsync(c->block, c->stream);
+  delete c;
+  if (e != hipSuccess) return hip_fail(e, "release: hipFreeAsync");
+  return SDM_ICL_OK;
+}
+
+sdm_icl_status sdm_icl_log_scale(const void* q, const void* gate, int32_t batch, int64_t rows,
+                                 int32_t heads, int32_t head_dim, int64_t key_length,
+                                 const float* head_coef, int32_t scale_mode,
+                                 const float* q_inv_scale, void* out, void* stream) {
+  if (batch < 1 || rows < 0 || heads < 1) return fail(SDM_ICL_E_INVALID, "log_scale: bad shape");
+  if (heads > kMaxHeads) return fail(SDM_ICL_E_UNSUPPORTED, "log_scale: at most %d heads", kMaxHeads);
+  if (head_dim != kHeadDim) return fail(SDM_ICL_E_UNSUPPORTED, "log_scale: head_dim must be 64");
+  if (key_length < 0) return fail(SDM_ICL_E_INVALID, "log_scale: key_length < 0");
+  if (scale_mode < SDM_ICL_SCALE_NONE || scale_mode > SDM_ICL_SCALE_GATED_LOG)
+    return fail(SDM_ICL_E_INVALID, "log_scale: unknown scale_mode %d", scale_mode);
+  if ((gate != nullptr) != (scale_mode == SDM_ICL_SCALE_GATED_LOG))
+    return fail(SDM_ICL_E_INVALID, "log_scale: gate must be given exactly when scale_mode is GATED_LOG");
+  if ((head_coef != nullptr) != (scale_mode != SDM_ICL_SCALE_NONE))
+    return fail(SDM_ICL_E_INVALID, "log_scale: head_coef must be given exactly when scale_mode is LOG or GATED_LOG");
+  if (rows == 0) return SDM_ICL_OK;
+  if (!q || !out) return fail(SDM_ICL_E_INVALID, "log_scale: q and out are required");
+  int dev;
+  DeviceInfo di;
+  sdm_icl_status st = current_device(&dev, &di);
+  if (st) return st;
+  const void* ptrs[] = {q, gate, out, q_inv_scale};
+  const char* names[] = {"q", "gate", "out", "q_inv_scale"};
+  for (int i = 0; i < 4; ++i)
+    if (ptrs[i] && (st = check_device_ptr(ptrs[i], dev, names[i]))) return st;
+  HeadFactors kh;
+  if (scale_mode != SDM_ICL_SCALE_NONE) head_factors(key_length, head_coef, heads, &kh);
+  else std::memset(&kh, 0, sizeof kh);
+  hipError_t e = launch_scale_queries((const uint16_t*)q, (const uint16_t*)gate, batch, rows, rows, rows,
+                                      heads, scale_mode, kh, q_inv_scale, out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "log_scale: launch");
+  return SDM_ICL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,144 @@
+"""Host-side tests of the C-ABI library (no GPU needed).
+
+The library must load and export every function that include/sdm_icl_attn.h
+declares; the host helpers (length scalar, fp16 head factors, precision rule,
+split plan) must agree with the oracle; and argument errors must be reported
+before anything touches a device.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from long_context_tabular_amd import binding as B
+from oracle import icl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdm_icl_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="library not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sdm_icl_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert len(names) >= 13, names
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"missing export {n}"
+    assert set(names) == set(B._SIGNATURES), "binding and header disagree"
+    assert B.sdm_icl_version() == 100
+
+
+@pytest.mark.parametrize("n", [0, 1, 2, 3, 1000, 1024, 8192, 16384, 65537, 131072, 523288, 524288, 10**9])
+def test_length_scalar_matches_oracle(n):
+    assert B.sdm_icl_length_scalar(n) == icl.length_scalar(n)
+
+
+def test_head_factors_match_oracle():
+    rng = np.random.default_rng(7)
+    for n in (1, 2, 1024, 16384, 131072, 523288, 524288):
+        for scale in (1.0, 1e-3, 1e-6, 100.0, 5000.0):
+            coef = (rng.uniform(0.5, 1.5, 128) * scale).astype(np.float32)
+            got = B.sdm_icl_head_factors(n, coef)
+            want = icl.head_factors(icl.length_scalar(n), coef)
+            np.testing.assert_array_equal(got.view(np.uint16), want.view(np.uint16))
+    # ties and overflow at the fp16 edges (L = ln 2 ... via n = 2: L = fp32(ln 2))
+    L = float(icl.length_scalar(2))
+    edge = np.array([65504.0, 65519.0, 65520.0, 1e6, 2.0 ** -24, 2.0 ** -25, 1.5 * 2.0 ** -24,
+                     3 * 2.0 ** -26, 1.0 + 2.0 ** -11, 1.0 + 3 * 2.0 ** -11], dtype=np.float64) / L
+    coef = edge.astype(np.float32)
+    np.testing.assert_array_equal(B.sdm_icl_head_factors(2, coef).view(np.uint16),
+                                  icl.head_factors(icl.length_scalar(2), coef).view(np.uint16))
+
+
+def test_precision_rule_matches_oracle():
+    for n in (1, 8191, 8192, 8193, 10**6):
+        for req in (0, 1, 2):
+            assert B.sdm_icl_select_precision(n, req) == icl.select_precision(n, req)
+
+
+def test_split_plan_is_a_function_of_n_only():
+    for n in (1, 63, 64, 65, 1000, 16384, 131072, 523288, 524288):
+        s, kps = B.sdm_icl_split_plan(n, 256)
+        assert kps % 64 == 0 and s >= 1
+        assert (s - 1) * kps < n <= s * kps   # every split holds at least one valid key
+    assert B.sdm_icl_split_plan(524288, 256) == (64, 8192)
+    with pytest.raises(B.SdmIclError):
+        B.sdm_icl_split_plan(0, 256)
+
+
+def _fit_args(**kw):
+    lengths = (ctypes.c_int64 * 1)(100)
+    coef = (ctypes.c_float * 8)(*([1.0] * 8))
+    base = dict(batch=1, rows_padded=128, heads=8, head_dim=64, lengths=lengths,
+                q=0x1000, k=0x2000, v=0x3000, gate=None, head_coef=None, scale_mode=0,
+                precision=0, out_ctx=None, stream=None)
+    base.update(kw)
+    if base.get("head_coef") == "set":
+        base["head_coef"] = coef
+    return B.FitArgs(**base), (lengths, coef)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), 1),
+    (dict(heads=0), 1),
+    (dict(heads=129), 2),
+    (dict(head_dim=128), 2),
+    (dict(lengths=None), 1),
+    (dict(q=None), 1),
+    (dict(scale_mode=3), 1),
+    (dict(scale_mode=1), 1),                           # LOG without coefficients
+    (dict(scale_mode=2, head_coef="set"), 1),          # GATED without gate
+    (dict(scale_mode=0, gate=0x4000), 1),              # gate without GATED
+    (dict(scale_mode=0, head_coef="set"), 1),          # coefficients without scaling
+    (dict(precision=5), 1),
+    (dict(rows_padded=50), 1),                         # n = 100 > N_pad
+])
+def test_fit_rejects_bad_arguments_before_any_device_work(kw, status):
+    args, keep = _fit_args(**kw)
+    h = ctypes.c_void_p()
+    st = B.lib().sdm_icl_attn_fit(ctypes.byref(args), ctypes.byref(h))
+    assert st == status, B.sdm_icl_last_error()
+    assert h.value is None
+    assert B.sdm_icl_last_error()
+
+
+def test_per_batch_lengths_are_unsupported_and_zero_length_invalid():
+    lengths = (ctypes.c_int64 * 2)(100, 90)
+    args, keep = _fit_args(batch=2, lengths=lengths)
+    h = ctypes.c_void_p()
+    assert B.lib().sdm_icl_attn_fit(ctypes.byref(args), ctypes.byref(h)) == 2
+    lengths0 = (ctypes.c_int64 * 1)(0)
+    args, keep = _fit_args(lengths=lengths0)
+    assert B.lib().sdm_icl_attn_fit(ctypes.byref(args), ctypes.byref(h)) == 1
+
+
+def test_unknown_handles_are_rejected():
+    lib = B.lib()
+    bogus = ctypes.c_void_p(0xDEADBEEF)
+    size = ctypes.c_size_t()
+    assert lib.sdm_icl_attn_query_workspace_size(bogus, 10, ctypes.byref(size)) == 6
+    assert lib.sdm_icl_attn_query(bogus, None, None, 0, None, None, 0, None) == 6
+    assert lib.sdm_icl_attn_release(bogus) == 6
+    assert lib.sdm_icl_attn_release(None) == 6
+    info = B.CacheInfo()
+    assert lib.sdm_icl_attn_cache_info(bogus, ctypes.byref(info)) == 6
+
+
+def test_log_scale_validation():
+    lib = B.lib()
+    coef = (ctypes.c_float * 8)(*([1.0] * 8))
+    # GATED without gate, LOG without coef, bad head_dim
+    assert lib.sdm_icl_log_scale(0x1000, None, 1, 4, 8, 64, 10, coef, 2, None, 0x2000, None) == 1
+    assert lib.sdm_icl_log_scale(0x1000, None, 1, 4, 8, 64, 10, None, 1, None, 0x2000, None) == 1
+    assert lib.sdm_icl_log_scale(0x1000, None, 1, 4, 8, 32, 10, coef, 1, None, 0x2000, None) == 2
+    # zero rows is a no-op
+    assert lib.sdm_icl_log_scale(None, None, 1, 0, 8, 64, 10, coef, 1, None, None, None) == 0
