@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Throughput of row-wise ICL attention on one MI355X.
+
+One step = one model call on the 512K-row FP8 workload: fit (FP8 scales,
+K/V pack, scaled-query quantisation, context self-attention written to
+out_ctx) + a 1,024-row query against the cache + cache release.  Inputs are
+resident in HBM before the timed region.  value = algorithmic TFLOP/s of the
+step, 4 n^2 D H + 4 R n D H with n the valid (unmasked) rows.
+
+Also reported, on the 512K-row FP8 GatedLogScale cache: cached-prediction
+GB/s of 128-row query batches (algorithmic bytes: the K/V codes once plus the
+query rows, gate and outputs) and TFLOP/s of a 1,024-row batch; the roofline
+of the dominant kernel (the context attention) from HIP events recorded
+around its launches on its own stream during the timed region; and the
+float64 oracle timed on this host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA
+PEAK_FP16_TFLOPS = 2500.0    # MI355X dense FP16 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("attention.hip", "prep.hip"):
+        with open(os.path.join(ROOT, "long_context_tabular_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(kernel: str):
+    """HBM bytes per launch measured with rocprofv3 counters for this exact
+    kernel source, or None if no measurement matches the current source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def dev(a):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def bench_model_call(B, gen, w, steps, warmup):
+    import torch
+    x = gen.make_inputs(w)
+    gated = w.scale_mode == gen.SCALE_GATED_LOG
+    q, k, v = dev(x.q_ctx), dev(x.k_ctx), dev(x.v_ctx)
+    gate = dev(x.gate_ctx) if gated else None
+    coef = x.head_coef if w.scale_mode != gen.SCALE_NONE else None
+    qq = dev(x.q_query)
+    gq = dev(x.gate_query) if gated else None
+    out = torch.empty_like(q)
+    qout = torch.empty_like(qq)
+    c = B.sdm_icl_attn_fit(q, k, v, w.n_valid, w.scale_mode, w.precision, coef, gate, None)
+    info = c.info()
+    ws = torch.empty(B.sdm_icl_attn_query_workspace_size(c, w.n_query), dtype=torch.uint8, device="cuda")
+    c.release()
+
+    def step():
+        cache = B.sdm_icl_attn_fit(q, k, v, w.n_valid, w.scale_mode, w.precision, coef, gate, out)
+        B.sdm_icl_attn_query(cache, qq, gq, out=qout, workspace=ws)
+        cache.release()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    B.sdm_icl_timing_enable(True)
+    for cls in range(5):
+        B.sdm_icl_timing_read(cls)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    timings = {name: B.sdm_icl_timing_read(cls) for name, cls in
+               (("context", B.SDM_ICL_TIMING_CONTEXT), ("query", B.SDM_ICL_TIMING_QUERY),
+                ("combine", B.SDM_ICL_TIMING_COMBINE), ("scale", B.SDM_ICL_TIMING_SCALE),
+                ("prep", B.SDM_ICL_TIMING_PREP))}
+    B.sdm_icl_timing_enable(False)
+    return x, info, (t1 - t0) / steps, timings
+
+
+def bench_cached(B, gen, w, reps):
+    import numpy as np
+    import torch
+    x = gen.make_inputs(w)
+    gated = w.scale_mode == gen.SCALE_GATED_LOG
+    q, k, v = dev(x.q_ctx), dev(x.k_ctx), dev(x.v_ctx)
+    gate = dev(x.gate_ctx) if gated else None
+    cache = B.sdm_icl_attn_fit(q, k, v, w.n_valid, w.scale_mode, w.precision, x.head_coef, gate, None)
+    del q, k, v, gate
+    qq = dev(x.q_query)
+    gq = dev(x.gate_query) if gated else None
+    res = {}
+    for R in w.query_batches:
+        ws = torch.empty(B.sdm_icl_attn_query_workspace_size(cache, R), dtype=torch.uint8, device="cuda")
+        qb = qq[:, :R].contiguous()
+        gb = gq[:, :R].contiguous() if gq is not None else None
+        ob = torch.empty_like(qb)
+        for _ in range(10):
+            B.sdm_icl_attn_query(cache, qb, gb, out=ob, workspace=ws)
+        torch.cuda.synchronize()
+        B.sdm_icl_timing_enable(True)
+        for cls in range(5):
+            B.sdm_icl_timing_read(cls)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in evs:
+            a.record()
+            B.sdm_icl_attn_query(cache, qb, gb, out=ob, workspace=ws)
+            b.record()
+        torch.cuda.synchronize()
+        kq_ms, kq_n = B.sdm_icl_timing_read(B.SDM_ICL_TIMING_QUERY)
+        B.sdm_icl_timing_enable(False)
+        times = sorted(a.elapsed_time(b) for a, b in evs)
+        med = times[len(times) // 2]
+        n, H, D = w.n_valid, w.heads, w.head_dim
+        alg_bytes = 2 * n * H * D + R * H * D * 2 * 2 + (R * H * 2 if gated else 0)
+        flops = 4.0 * R * n * D * H
+        res[R] = {"us_median": med * 1e3, "us_min": times[0] * 1e3, "us_max": times[-1] * 1e3,
+                  "GB_per_s": alg_bytes / (med * 1e-3) / 1e9, "TFLOP_per_s": flops / (med * 1e-3) / 1e12,
+                  "attention_kernel_us": kq_ms / max(kq_n, 1) * 1e3,
+                  "attention_kernel_GB_per_s": alg_bytes / (kq_ms / max(kq_n, 1) * 1e-3) / 1e9,
+                  "algorithmic_bytes": alg_bytes}
+    info = cache.info()
+    cache.release()
+    return res, info
+
+
+def cpu_baseline(gen, x, w, sample_rows: int):
+    """The float64 oracle (as it stands) on a bounded sample of the same workload."""
+    import numpy as np
+    from oracle import icl
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    gated = w.scale_mode == gen.SCALE_GATED_LOG
+    t_fit0 = time.perf_counter()
+    cache = icl.fit(x.q_ctx, x.k_ctx, x.v_ctx, w.n_valid, w.scale_mode, w.precision,
+                    x.head_coef if w.scale_mode != gen.SCALE_NONE else None,
+                    x.gate_ctx if gated else None)
+    t_fit = time.perf_counter() - t_fit0
+    rows = gen.sample_rows(w.n_valid, sample_rows, w.seed)
+    qrows = np.arange(sample_rows)
+    t0 = time.perf_counter()
+    icl.context_outputs(cache, x.q_ctx, x.gate_ctx if gated else None, rows)
+    icl.attend(cache, x.q_query[0, qrows], x.gate_query[0, qrows] if gated else None)
+    dt = time.perf_counter() - t0
+    flops = 4.0 * (rows.size + qrows.size) * w.n_valid * w.head_dim * w.heads
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(dt, 3), "fit_seconds_untimed": round(t_fit, 3),
+            "host_cpus": len(os.sched_getaffinity(0)),
+            "sample": (f"{rows.size} context rows (incl. first/last 8 valid) + {qrows.size} query rows of "
+                       f"{w.name}, each against all {w.n_valid} keys x {w.heads} heads, float64; the "
+                       f"oracle's fit (scales + e4m3 codes of all K/V, {t_fit:.1f} s) ran before the timed part")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="model512k_fp8_log")
+    ap.add_argument("--cached-workload", default="cached512k_fp8_gated")
+    ap.add_argument("--cached-reps", type=int, default=30)
+    ap.add_argument("--no-cached", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=32)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this engine runs on a single MI355X "
+              "(multi-GPU sharding is a design note, not an implemented path).", file=sys.stderr)
+        return 2
+
+    import torch
+    from long_context_tabular_amd import binding as B
+    from long_context_tabular_amd import inputs as gen
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    B.lib()
+
+    w = gen.WORKLOADS[args.workload]
+    log(f"[bench] model call {w.name}: n_pad={w.n_pad} n={w.n_valid} R={w.n_query} H={w.heads}")
+    x, info, sec, t = bench_model_call(B, gen, w, args.steps, args.warmup)
+    n, H, D, R = w.n_valid, w.heads, w.head_dim, w.n_query
+    ctx_flops = 4.0 * n * n * D * H
+    q_flops = 4.0 * R * n * D * H
+    value = (ctx_flops + q_flops) / sec / 1e12
+    ctx_ms, ctx_n = t["context"]
+    ctx_avg = ctx_ms / max(ctx_n, 1)
+    achieved = ctx_flops / (ctx_avg * 1e-3) / 1e12
+    prec_name = "fp8_e4m3" if info["precision"] == 1 else "fp16"
+    peak = PEAK_FP8_TFLOPS if info["precision"] == 1 else PEAK_FP16_TFLOPS
+    log(f"[bench] step {sec * 1e3:.2f} ms, {value:.1f} TFLOP/s; context kernel {ctx_avg:.3f} ms "
+        f"({achieved:.1f} TFLOP/s)")
+    line = {
+        "metric": "ICL attention TFLOP/s at 128K-512K context rows (% MFMA peak); cached GB/s",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": prec_name,
+        "data": "synthetic",
+        "config": {"workload": w.name, "n_pad": w.n_pad, "n_valid": n, "n_query": R, "heads": H,
+                   "head_dim": D, "precision": prec_name, "scale": ["none", "log", "gated_log"][w.scale_mode],
+                   "qk_operands": prec_name, "pv_operands": "fp16", "softmax": "fp32",
+                   "kv_splits": info["kv_splits"]},
+        "roofline": {"bound": "mfma", "kernel": "attention_kernel (context pass)",
+                     "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": counter_traffic("context"),
+                     "launch_ms": round(ctx_avg, 4), "launches": ctx_n},
+        "step_breakdown_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in t.items() if v[1]},
+    }
+    if not args.no_cached:
+        wc = gen.WORKLOADS[args.cached_workload]
+        log(f"[bench] cached prediction {wc.name}: n={wc.n_valid} batches {wc.query_batches}")
+        cres, cinfo = bench_cached(B, gen, wc, args.cached_reps)
+        r128 = cres.get(128)
+        line["cached"] = {"workload": wc.name, "kv_splits": cinfo["kv_splits"],
+                          "GB_per_s": round(r128["GB_per_s"], 1) if r128 else None,
+                          "hbm_frac": round(r128["GB_per_s"] / PEAK_HBM_GBS, 4) if r128 else None,
+                          "batches": {str(k): {kk: (round(vv, 3) if isinstance(vv, float) else vv)
+                                               for kk, vv in v.items()} for k, v in cres.items()}}
+        log(f"[bench] cached: {json.dumps(line['cached'])}")
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (float64 oracle)")
+        line["cpu_baseline"] = cpu_baseline(gen, x, w, args.cpu_sample_rows)
+    torch.cuda.synchronize()
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

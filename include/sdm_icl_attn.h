@@ -163,6 +163,26 @@ sdm_icl_status sdm_icl_log_scale(const void* q, const void* gate, int32_t batch,
                                  const float* head_coef, int32_t scale_mode,
                                  const float* q_inv_scale, void* out, void* stream);
 
+/* ---- kernel timing (observability) -------------------------------------
+ * When enabled, each kernel launch of the library is bracketed by two HIP
+ * events recorded on the launch's own stream, grouped by kernel class:
+ *   SDM_ICL_TIMING_CONTEXT  context self-attention (fit with out_ctx)
+ *   SDM_ICL_TIMING_QUERY    cached-query split-KV attention
+ *   SDM_ICL_TIMING_COMBINE  split combine
+ *   SDM_ICL_TIMING_SCALE    fused q-scale (+quantise)
+ *   SDM_ICL_TIMING_PREP     fit preparation (amax, scales, K/V pack)
+ * Off by default; enabling adds two event records per launch.
+ * sdm_icl_timing_read waits for the recorded events of one class, returns
+ * their summed duration in milliseconds and the launch count, and clears
+ * that class. */
+#define SDM_ICL_TIMING_CONTEXT 0
+#define SDM_ICL_TIMING_QUERY   1
+#define SDM_ICL_TIMING_COMBINE 2
+#define SDM_ICL_TIMING_SCALE   3
+#define SDM_ICL_TIMING_PREP    4
+sdm_icl_status sdm_icl_timing_enable(int32_t on);
+sdm_icl_status sdm_icl_timing_read(int32_t kernel_class, double* total_ms, int64_t* launches);
+
 /* ---- host-only helpers (no device work; usable without a GPU) ---------- */
 
 /* L32 = fp32(ln(max(n, 1))). */

@@ -67,6 +67,9 @@ _SIGNATURES = {
                                            ctypes.c_int64, ctypes.POINTER(ctypes.c_float),
                                            ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_void_p]),
+    "sdm_icl_timing_enable": (ctypes.c_int32, [ctypes.c_int32]),
+    "sdm_icl_timing_read": (ctypes.c_int32, [ctypes.c_int32, ctypes.POINTER(ctypes.c_double),
+                                             ctypes.POINTER(ctypes.c_int64)]),
     "sdm_icl_length_scalar": (ctypes.c_float, [ctypes.c_int64]),
     "sdm_icl_head_factors": (ctypes.c_int32, [ctypes.c_int64, ctypes.POINTER(ctypes.c_float),
                                               ctypes.c_int32, ctypes.POINTER(ctypes.c_uint16)]),
@@ -150,6 +153,22 @@ def sdm_icl_split_plan(n: int, num_cus: int):
     k = ctypes.c_int64()
     _check(lib().sdm_icl_split_plan(int(n), int(num_cus), ctypes.byref(s), ctypes.byref(k)))
     return s.value, k.value
+
+
+SDM_ICL_TIMING_CONTEXT, SDM_ICL_TIMING_QUERY, SDM_ICL_TIMING_COMBINE = 0, 1, 2
+SDM_ICL_TIMING_SCALE, SDM_ICL_TIMING_PREP = 3, 4
+
+
+def sdm_icl_timing_enable(on: bool) -> None:
+    _check(lib().sdm_icl_timing_enable(1 if on else 0))
+
+
+def sdm_icl_timing_read(kernel_class: int):
+    """(summed milliseconds, launches) of one kernel class since the last read."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check(lib().sdm_icl_timing_read(int(kernel_class), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 # ------------------------------------------------------------------ cache handle

@@ -159,6 +159,44 @@ bool live(const sdm_icl_cache_s* c) {
   return c != nullptr && g_registry.count(c) != 0 && c->magic == kMagic;
 }
 
+// ---- kernel timing: event pairs around launches, per kernel class
+constexpr int kTimingClasses = 5;
+struct TimingRec {
+  int cls;
+  hipEvent_t a, b;
+};
+std::mutex g_timing_mu;
+bool g_timing_on = false;
+std::vector<TimingRec> g_timing;
+
+struct TimedLaunch {
+  bool on = false;
+  TimingRec rec{};
+  hipStream_t s;
+  TimedLaunch(int cls, hipStream_t stream) : s(stream) {
+    {
+      std::lock_guard<std::mutex> lk(g_timing_mu);
+      on = g_timing_on;
+    }
+    if (!on) return;
+    rec.cls = cls;
+    if (hipEventCreate(&rec.a) != hipSuccess || hipEventCreate(&rec.b) != hipSuccess ||
+        hipEventRecord(rec.a, s) != hipSuccess) {
+      (void)hipGetLastError();
+      on = false;
+    }
+  }
+  ~TimedLaunch() {
+    if (!on) return;
+    if (hipEventRecord(rec.b, s) != hipSuccess) {
+      (void)hipGetLastError();
+      return;
+    }
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    g_timing.push_back(rec);
+  }
+};
+
 struct QueryLayout {
   size_t q_off, po_off, ml_off, total;
   int64_t q_rows_alloc;
@@ -312,17 +350,23 @@ sdm_icl_status sdm_icl_attn_fit(const sdm_icl_fit_args* a, sdm_icl_cache* out) {
   auto g16 = (const uint16_t*)a->gate;
 
   if (prec == SDM_ICL_PREC_FP8_E4M3) {
+    TimedLaunch tl(SDM_ICL_TIMING_PREP, s);
     e = launch_fp8_scales(q16, k16, v16, g16, B, a->rows_padded, n, H, a->scale_mode, c->kh, amax,
                           c->scales, c->inv, s);
   } else {
     e = launch_fill_f32(c->scales, 6 * (int64_t)B * H, 1.0f, s);
   }
-  if (e == hipSuccess)
+  if (e == hipSuccess) {
+    TimedLaunch tl(SDM_ICL_TIMING_PREP, s);
     e = launch_pack_kv(k16, v16, B, a->rows_padded, n, c->n_alloc, H, prec, c->inv + B * H,
                        c->inv + 2 * B * H, c->kc, c->vt, s);
+  }
   if (e == hipSuccess && a->out_ctx) {
-    e = launch_scale_queries(q16, g16, B, a->rows_padded, n, q_rows_alloc, H, a->scale_mode, c->kh,
-                             prec == SDM_ICL_PREC_FP8_E4M3 ? c->inv : nullptr, qctx, s);
+    {
+      TimedLaunch tl(SDM_ICL_TIMING_SCALE, s);
+      e = launch_scale_queries(q16, g16, B, a->rows_padded, n, q_rows_alloc, H, a->scale_mode, c->kh,
+                               prec == SDM_ICL_PREC_FP8_E4M3 ? c->inv : nullptr, qctx, s);
+    }
     if (e == hipSuccess) {
       AttnArgs at = attn_args(c);
       at.q = qctx;
@@ -332,6 +376,7 @@ sdm_icl_status sdm_icl_attn_fit(const sdm_icl_fit_args* a, sdm_icl_cache* out) {
       at.out = (uint16_t*)a->out_ctx;
       at.splits = 1;
       at.tiles_per_split = (int32_t)(c->n_alloc / kKeyTile);
+      TimedLaunch tl(SDM_ICL_TIMING_CONTEXT, s);
       e = launch_attention(at, prec, false, s);
     }
   }
@@ -387,9 +432,13 @@ sdm_icl_status sdm_icl_attn_query(sdm_icl_cache c, const void* q, const void* ga
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
   void* qbuf = w + L.q_off;
-  hipError_t e = launch_scale_queries((const uint16_t*)q, (const uint16_t*)gate, c->B, R, R, L.q_rows_alloc,
-                                      c->H, c->mode, c->kh,
-                                      c->prec == SDM_ICL_PREC_FP8_E4M3 ? c->inv : nullptr, qbuf, s);
+  hipError_t e;
+  {
+    TimedLaunch tl(SDM_ICL_TIMING_SCALE, s);
+    e = launch_scale_queries((const uint16_t*)q, (const uint16_t*)gate, c->B, R, R, L.q_rows_alloc,
+                             c->H, c->mode, c->kh,
+                             c->prec == SDM_ICL_PREC_FP8_E4M3 ? c->inv : nullptr, qbuf, s);
+  }
   if (e != hipSuccess) return hip_fail(e, "query: scale launch");
   AttnArgs at = attn_args(c);
   at.q = qbuf;
@@ -401,12 +450,18 @@ sdm_icl_status sdm_icl_attn_query(sdm_icl_cache c, const void* q, const void* ga
   if (c->splits > 1) {
     at.part_o = (float*)(w + L.po_off);
     at.part_ml = (float*)(w + L.ml_off);
-    e = launch_attention(at, c->prec, true, s);
-    if (e == hipSuccess)
+    {
+      TimedLaunch tl(SDM_ICL_TIMING_QUERY, s);
+      e = launch_attention(at, c->prec, true, s);
+    }
+    if (e == hipSuccess) {
+      TimedLaunch tl(SDM_ICL_TIMING_COMBINE, s);
       e = launch_combine(at.part_o, at.part_ml, c->scales + 2 * c->B * c->H, c->B, c->H, R, c->splits,
                          c->prec, (uint16_t*)out, s);
+    }
   } else {
     at.out = (uint16_t*)out;
+    TimedLaunch tl(SDM_ICL_TIMING_QUERY, s);
     e = launch_attention(at, c->prec, false, s);
   }
   if (e != hipSuccess) return hip_fail(e, "query: attention launch");
@@ -485,6 +540,39 @@ sdm_icl_status sdm_icl_attn_release(sdm_icl_cache c) {
   return SDM_ICL_OK;
 }
 
+sdm_icl_status sdm_icl_timing_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  g_timing_on = on != 0;
+  return SDM_ICL_OK;
+}
+
+sdm_icl_status sdm_icl_timing_read(int32_t cls, double* total_ms, int64_t* launches) {
+  if (!total_ms || !launches) return fail(SDM_ICL_E_INVALID, "timing_read: null pointer");
+  if (cls < 0 || cls >= kTimingClasses) return fail(SDM_ICL_E_INVALID, "timing_read: unknown class %d", cls);
+  std::vector<TimingRec> mine;
+  {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    std::vector<TimingRec> rest;
+    for (const TimingRec& r : g_timing) (r.cls == cls ? mine : rest).push_back(r);
+    g_timing.swap(rest);
+  }
+  double sum = 0;
+  hipError_t err = hipSuccess;
+  for (const TimingRec& r : mine) {
+    float ms = 0;
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess && err == hipSuccess) err = e;
+    sum += ms;
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  if (err != hipSuccess) return hip_fail(err, "timing_read");
+  *total_ms = sum;
+  *launches = (int64_t)mine.size();
+  return SDM_ICL_OK;
+}
+
 sdm_icl_status sdm_icl_log_scale(const void* q, const void* gate, int32_t batch, int64_t rows,
                                  int32_t heads, int32_t head_dim, int64_t key_length,
                                  const float* head_coef, int32_t scale_mode,
@@ -512,6 +600,7 @@ sdm_icl_status sdm_icl_log_scale(const void* q, const void* gate, int32_t batch,
   HeadFactors kh;
   if (scale_mode != SDM_ICL_SCALE_NONE) head_factors(key_length, head_coef, heads, &kh);
   else std::memset(&kh, 0, sizeof kh);
+  TimedLaunch tl(SDM_ICL_TIMING_SCALE, (hipStream_t)stream);
   hipError_t e = launch_scale_queries((const uint16_t*)q, (const uint16_t*)gate, batch, rows, rows, rows,
                                       heads, scale_mode, kh, q_inv_scale, out, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "log_scale: launch");

@@ -11,13 +11,18 @@ width of 8 heads x 64.  Values are N(0,1)/8 in fp16; the FP8 workloads add
 0.1% outliers at +-20 sigma; a padded context tail is filled with NaN so that
 any read of a masked row shows up in the output.
 
-Draw order (fixed, per config): context Q, K, V ``[B, N_pad, H, D]``; query Q
-``[B, R, H, D]``; head coefficients ``[H]`` ~ U(0.5, 1.5) (float32); context
-gate ``[B, N_pad, H]`` and query gate ``[B, R, H]`` ~ N(0, 1) (fp16); then, if
-outliers are on, one outlier mask and sign per tensor in the same order.
+Streams (fixed, per config seed): context Q, K, V ``[B, N_pad, H, D]`` and
+query Q ``[B, R, H, D]`` come from per-64K-row-chunk generators keyed by
+(seed, tensor index 0..3, batch, chunk); from ``default_rng(seed)``, in order:
+head coefficients ``[H]`` ~ U(0.5, 1.5) (float32), context gate
+``[B, N_pad, H]`` and query gate ``[B, R, H]`` ~ N(0, 1) (fp16), then, if
+outliers are on, an outlier count, positions and signs per tensor in the order
+context Q, K, V, query Q.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field, replace
 from typing import Dict, Optional
 
@@ -102,29 +107,38 @@ def scaled_down(w: Workload, n_pad: int, n_valid: Optional[int] = None,
                    n_query=w.n_query if n_query is None else n_query)
 
 
-def _normal_fp16(rng: np.random.Generator, shape) -> np.ndarray:
-    """N(0,1)/8 drawn as float32 and rounded (nearest-even) to fp16, in row chunks."""
+def _normal_fp16(seed: int, tensor: int, shape) -> np.ndarray:
+    """N(0,1)/8 drawn as float32 and rounded (nearest-even) to fp16.
+
+    Each 64K-row chunk has its own generator, seeded from (seed, tensor,
+    batch, chunk) through numpy's SeedSequence, so chunks are drawn in
+    parallel threads and the result does not depend on the thread count."""
     out = np.empty(shape, dtype=np.float16)
     rows = shape[1]
-    for b in range(shape[0]):
-        for r0 in range(0, rows, _CHUNK_ROWS):
-            r1 = min(rows, r0 + _CHUNK_ROWS)
-            sub = (r1 - r0,) + tuple(shape[2:])
-            out[b, r0:r1] = (rng.standard_normal(sub, dtype=np.float32) / np.float32(8.0)).astype(np.float16)
+    jobs = [(b, r0) for b in range(shape[0]) for r0 in range(0, rows, _CHUNK_ROWS)]
+
+    def fill(job):
+        b, r0 = job
+        r1 = min(rows, r0 + _CHUNK_ROWS)
+        sub = (r1 - r0,) + tuple(shape[2:])
+        g = np.random.Generator(np.random.PCG64(
+            np.random.SeedSequence(seed, spawn_key=(tensor, b, r0 // _CHUNK_ROWS))))
+        out[b, r0:r1] = (g.standard_normal(sub, dtype=np.float32) / np.float32(8.0)).astype(np.float16)
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), len(jobs)))
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        list(pool.map(fill, jobs))
     return out
 
 
 def _add_outliers(rng: np.random.Generator, x: np.ndarray) -> None:
-    """Replace a 1e-3 fraction of elements by +-20 sigma (= +-2.5), in place."""
-    rows = x.shape[1]
-    for b in range(x.shape[0]):
-        for r0 in range(0, rows, _CHUNK_ROWS):
-            r1 = min(rows, r0 + _CHUNK_ROWS)
-            sub = (r1 - r0,) + tuple(x.shape[2:])
-            mask = rng.random(sub) < 1e-3
-            sign = np.where(rng.random(sub) < 0.5, -1.0, 1.0)
-            blk = x[b, r0:r1]
-            blk[mask] = (2.5 * sign[mask]).astype(np.float16)
+    """Set a Binomial(size, 1e-3) number of elements, at uniformly drawn
+    positions (with replacement), to +-20 sigma (= +-2.5) with random signs."""
+    flat = x.reshape(-1)
+    count = int(rng.binomial(flat.size, 1e-3))
+    pos = rng.integers(0, flat.size, size=count)
+    sign = rng.integers(0, 2, size=count) * 2 - 1
+    flat[pos] = (2.5 * sign).astype(np.float16)
 
 
 @dataclass
@@ -146,10 +160,10 @@ def make_inputs(w: Workload) -> Inputs:
     """Draw every tensor of workload ``w`` from ``numpy.random.default_rng(w.seed)``."""
     rng = np.random.default_rng(w.seed)
     B, N, H, D, R = w.batch, w.n_pad, w.heads, w.head_dim, w.n_query
-    q_ctx = _normal_fp16(rng, (B, N, H, D))
-    k_ctx = _normal_fp16(rng, (B, N, H, D))
-    v_ctx = _normal_fp16(rng, (B, N, H, D))
-    q_query = _normal_fp16(rng, (B, R, H, D))
+    q_ctx = _normal_fp16(w.seed, 0, (B, N, H, D))
+    k_ctx = _normal_fp16(w.seed, 1, (B, N, H, D))
+    v_ctx = _normal_fp16(w.seed, 2, (B, N, H, D))
+    q_query = _normal_fp16(w.seed, 3, (B, R, H, D))
     head_coef = rng.uniform(0.5, 1.5, size=H).astype(np.float32)
     gate_ctx = rng.standard_normal((B, N, H), dtype=np.float32).astype(np.float16)
     gate_query = rng.standard_normal((B, R, H), dtype=np.float32).astype(np.float16)

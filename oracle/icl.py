@@ -78,7 +78,18 @@ def scale_queries(q: np.ndarray, mode: int, k_h: Optional[np.ndarray],
     if mode == SCALE_NONE:
         return q.copy()
     kh = np.asarray(k_h, dtype=np.float16).astype(np.float32)[:, None]
-    qk = (q.astype(np.float32) * kh).astype(np.float16)
+    if q.size >= (1 << 20):
+        # fp16(q * k_h) depends only on q's 16-bit pattern for a given head:
+        # evaluate the same expression once per pattern and index it
+        allx = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float32)
+        qk = np.empty_like(q)
+        bits = q.view(np.uint16)
+        for h in range(q.shape[-2]):
+            with np.errstate(over="ignore", invalid="ignore"):   # inf/NaN patterns
+                table = (allx * kh[h, 0]).astype(np.float16)
+            qk[..., h, :] = table[bits[..., h, :]]
+    else:
+        qk = (q.astype(np.float32) * kh).astype(np.float16)
     if mode == SCALE_LOG:
         return qk
     if mode != SCALE_GATED_LOG:
@@ -108,8 +119,14 @@ def fp8_scale(amax) -> tuple:
 
 
 def amax_rows(x: np.ndarray) -> np.ndarray:
-    """max |x| over rows and head_dim for x ``[rows, H, D]`` -> ``[H]`` (fp16-exact)."""
-    return np.max(np.abs(x.astype(np.float64)), axis=(0, 2))
+    """max |x| over rows and head_dim for finite fp16 x ``[rows, H, D]`` -> ``[H]``.
+
+    For finite IEEE numbers, |x| orders exactly as the bit pattern with the
+    sign bit cleared, read as an unsigned integer; the maximum is taken on
+    those patterns and converted back, so it is exact."""
+    mag = np.asarray(x, dtype=np.float16).view(np.uint16) & np.uint16(0x7FFF)
+    top = mag.max(axis=2).max(axis=0).astype(np.uint16)
+    return top.view(np.float16).astype(np.float64)
 
 
 def quantize(x: np.ndarray, inv) -> np.ndarray:
@@ -119,9 +136,24 @@ def quantize(x: np.ndarray, inv) -> np.ndarray:
     return e4m3_round(y)
 
 
+def _code_table(inv) -> np.ndarray:
+    """quantize + encode evaluated once on every fp16 bit pattern (finite ones;
+    NaN/inf patterns map to 0 and never occur in valid rows)."""
+    x = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    ok = np.isfinite(x)
+    table = np.zeros(65536, dtype=np.uint8)
+    table[ok] = e4m3_encode(quantize(x[ok], inv))
+    return table
+
+
 def quantize_codes(x: np.ndarray, inv) -> np.ndarray:
-    """E4M3 bit patterns of :func:`quantize`."""
-    return e4m3_encode(quantize(x, inv))
+    """E4M3 bit patterns of :func:`quantize`.  x is fp16 and inv is one
+    float32, so the code is a function of x's 16-bit pattern: large inputs
+    index a table of that function instead of recomputing it per element."""
+    x = np.asarray(x, dtype=np.float16)
+    if x.size < 65536:
+        return e4m3_encode(quantize(x, inv))
+    return _code_table(inv)[x.view(np.uint16)]
 
 
 # ---------------------------------------------------------------------------

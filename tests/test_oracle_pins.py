@@ -288,3 +288,26 @@ def test_inputs_recipe():
     assert np.all((x.head_coef >= 0.5) & (x.head_coef <= 1.5))
     y = gen.make_inputs(w)
     np.testing.assert_array_equal(x.q_query, y.q_query)
+
+
+def test_amax_matches_float_maximum():
+    x = gen.make_inputs(gen.scaled_down(gen.WORKLOADS["ctx128k_fp8"], 2048)).v_ctx[0]
+    x[5, 2, 7] = np.float16(-3.0)            # a negative element holds the maximum
+    want = np.max(np.abs(x.astype(np.float64)), axis=(0, 2))
+    np.testing.assert_array_equal(icl.amax_rows(x), want)
+    assert icl.amax_rows(x)[2] == 3.0
+
+
+def test_large_input_shortcuts_equal_the_plain_expressions():
+    """The per-pattern tables used for large inputs evaluate the same
+    expressions as the element-wise path."""
+    w = gen.scaled_down(gen.WORKLOADS["model512k_fp8_log"], 1 << 15, n_query=4)
+    x = gen.make_inputs(w)
+    q = x.q_ctx[0, :w.n_valid]                 # valid rows (the masked tail is NaN)
+    kh = icl.head_factors(icl.length_scalar(1000), x.head_coef)
+    direct = (q.astype(np.float32) * kh.astype(np.float32)[:, None]).astype(np.float16)
+    np.testing.assert_array_equal(icl.scale_queries(q, icl.SCALE_LOG, kh).view(np.uint16), direct.view(np.uint16))
+    inv = icl.fp8_scale(float(icl.amax_rows(q)[0]))[1]
+    big = np.ascontiguousarray(q[:, 0, :])
+    assert big.size >= 65536
+    np.testing.assert_array_equal(icl.quantize_codes(big, inv), numerics.e4m3_encode(icl.quantize(big, inv)))
