@@ -15,15 +15,19 @@
 // Data flow of one workgroup (4 wavefronts, each owning QG x 32 query rows):
 //   * Q stays in VGPRs for the whole KV loop (MFMA B operand).
 //   * 64-key tiles of K and of V are fetched as separate loads into registers
-//     one tile ahead, and written into separate double-buffered LDS stages
+//     two tiles ahead, and written into separate double-buffered LDS stages
 //     (K row-major, V transposed and widened to fp16), one barrier per tile.
 //   * S^T = K Q^T with v_mfma_f32_32x32x64_f8f6f4 (FP8) or 32x32x16_f16.
 //     K rows are fed in a permuted order so that each lane ends up holding,
 //     for its own query, exactly the 8-key groups that the PV MFMA wants in
 //     its B operand: P never leaves registers.
-//   * Online softmax in base 2 (the scale is folded into one FMA per score),
-//     with a lazily moved reference maximum: O and l are rescaled only when a
-//     tile's maximum exceeds the reference by more than 8 (so p <= 256).
+//   * Online softmax in base 2 (the scale is folded into one FMA per score).
+//     The first tile of a wave's KV range sets each row's reference maximum;
+//     later tiles compute P against it with no per-tile max at all, and a row
+//     moves its reference (rescaling O and l) only when its 64 rounded P of a
+//     tile sum to more than 2^14, which bounds every P below fp16's range.
+//     Full tiles carry no masking code; the ragged last tile of the context
+//     is a separate instantiation.
 //   * O^T += V^T P^T with v_mfma_f32_32x32x16_f16; P is rounded to fp16
 //     (nearest even) and l is summed from the same rounded P (v_dot2).
 // Every per-row quantity depends only on that row's own scores, so a row's
@@ -48,7 +52,10 @@ typedef __fp16 h16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr float kRescaleThreshold = 8.0f;  // log2 units: p <= 2^8 between rescales
+// After a row's first tile, P is taken against a reference maximum that is
+// moved only when a tile's 64 rounded P values of that row sum to more than
+// this; every P then stays <= 2^14 (finite in fp16) without a per-tile max.
+constexpr float kMaxTileSum = 16384.0f;
 
 // Row r of a 32-row MFMA A operand holds key sigma(r) of its 32-key chunk:
 // bits 2 and 3 of r swapped.  With the 32x32 output layout (lane l, register
@@ -113,6 +120,120 @@ constexpr int kVRow = 144;  // LDS bytes per d-row of the fp16 V^T tile (128 + 1
 template <int EB>
 struct Stage { i32x4 k[EB]; i32x4 v[EB]; };
 
+// Per-wave running state: Q fragments, reference maxima (log2 units), row
+// sums of P and the O^T accumulators of QG groups of 32 query rows.
+template <int PREC, int QG>
+struct WaveState {
+  typename Ops<PREC>::QFrag qf[QG];
+  float m_run[QG], l_run[QG];
+  f32x16 o[QG][2];
+};
+
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
+  float mx = s[0][0];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[c][r]);
+  float lo, hi;
+  halves(mx, lo, hi);
+  return fmaxf(lo, hi);
+}
+
+// P = fp16(exp2(s * c - m)) for the lane's 32 scores; returns the fp32 sum of
+// the rounded P (v_dot2 of each packed fp16 pair with (1, 1)).
+__device__ __forceinline__ float exp_tile(const f32x16 (&s)[2], float c_scale, float neg_m,
+                                          f16x8 (&p16)[2][2]) {
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        p16[c][ks][e] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[c][8 * ks + e], c_scale, neg_m));
+  const h16x2 ones = {(__fp16)1.0f, (__fp16)1.0f};
+  float lsum = 0.f;
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const f16x8 pv = p16[c][ks];
+      const i32x4 words = __builtin_bit_cast(i32x4, pv);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // copy the element first: bit-casting a vector element directly
+        // reads element 0 with this compiler
+        const int word = words[i];
+        lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, word), ones, lsum, false);
+      }
+    }
+  return lsum;
+}
+
+// One 64-key tile for all QG groups of the wave.  FIRST: the first tile of
+// the wave's KV range, which sets the reference maximum.  MASK: the tile holds
+// keys >= n (only the last tile of the context can), 'rem' = n - tile start.
+template <int PREC, int QG, bool FIRST, bool MASK>
+__device__ __forceinline__ void attend_tile(WaveState<PREC, QG>& w, const unsigned char* kb,
+                                            const unsigned char* vb, float c_scale, int col,
+                                            int hf, int rem) {
+  typedef Ops<PREC> O;
+  // ---- S^T = K Q^T, two 32-key chunks
+  f32x16 s[QG][2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int g = 0; g < QG; ++g) s[g][c] = O::qk(kb + (32 * c + col) * O::KROW, hf, w.qf[g]);
+
+  // ---- softmax weights (base 2)
+  f16x8 p16[QG][2][2];
+#pragma unroll
+  for (int g = 0; g < QG; ++g) {
+    if constexpr (MASK) {
+      const int lim = rem - 8 * hf;  // key offset in the tile = 32c + 16(r/8) + 8hf + r%8
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * c + 16 * (r >> 3) + (r & 7) >= lim) s[g][c][r] = -INFINITY;
+    }
+    if constexpr (FIRST) w.m_run[g] = tile_max(s[g]) * c_scale;
+    float lt = exp_tile(s[g], c_scale, -w.m_run[g], p16[g]);
+    if constexpr (!FIRST) {
+      float lo, hi;
+      halves(lt, lo, hi);
+      const bool over = !(lo + hi <= kMaxTileSum);  // also true for inf
+      if (__builtin_amdgcn_ballot_w64(over) != 0) {  // rare, wave-uniform
+        // only rows that overflowed move their reference (others keep it
+        // bit for bit, so a row never depends on its neighbours)
+        const float mt = tile_max(s[g]) * c_scale;
+        const float mnew = over ? fmaxf(w.m_run[g], mt) : w.m_run[g];
+        const float alpha = __builtin_amdgcn_exp2f(w.m_run[g] - mnew);
+        w.m_run[g] = mnew;
+        w.l_run[g] *= alpha;
+        w.o[g][0] *= alpha;
+        w.o[g][1] *= alpha;
+        lt = exp_tile(s[g], c_scale, -mnew, p16[g]);
+      }
+    }
+    w.l_run[g] += lt;
+  }
+
+  // ---- O^T += V^T P^T
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) {
+        const f16x8 va = *reinterpret_cast<const f16x8*>(vb + (32 * dt + col) * kVRow +
+                                                         (32 * c + 16 * ks + 8 * hf) * 2);
+#pragma unroll
+        for (int g = 0; g < QG; ++g)
+          w.o[g][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, p16[g][c][ks], w.o[g][dt], 0, 0, 0);
+      }
+}
+
 template <int PREC, int QG, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
   typedef Ops<PREC> O;
@@ -152,11 +273,16 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
 
   // Q fragments for this wave's QG x 32 rows
   const unsigned char* qbase = reinterpret_cast<const unsigned char*>(a.q);
-  typename O::QFrag qf[QG];
+  WaveState<PREC, QG> ws;
   const int64_t wq0 = q0 + (int64_t)w * QG * 32;
 #pragma unroll
-  for (int g = 0; g < QG; ++g)
-    qf[g] = O::load_q(qbase + (((int64_t)bh * a.q_rows_alloc) + wq0 + g * 32 + col) * 64 * EB, hf);
+  for (int g = 0; g < QG; ++g) {
+    ws.qf[g] = O::load_q(qbase + (((int64_t)bh * a.q_rows_alloc) + wq0 + g * 32 + col) * 64 * EB, hf);
+    ws.m_run[g] = 0.f;
+    ws.l_run[g] = 0.f;
+    ws.o[g][0] = f32x16{};
+    ws.o[g][1] = f32x16{};
+  }
 
   const int64_t n_tiles = a.n_alloc / 64;
   const int64_t t0 = (int64_t)split * a.tiles_per_split;
@@ -202,134 +328,68 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
     }
   };
 
-  float m_run[QG], l_run[QG];
-  f32x16 o[QG][2];
-#pragma unroll
-  for (int g = 0; g < QG; ++g) {
-    m_run[g] = -INFINITY;
-    l_run[g] = 0.f;
-    o[g][0] = f32x16{};
-    o[g][1] = f32x16{};
-  }
-
-  Stage<EB> st;
-  load_stage(t0, st);
-  store_stage(0, st);
-  if (t0 + 1 < t1) load_stage(t0 + 1, st);
+  // Two staging register sets, each loaded two tiles ahead: while tile t is
+  // processed, the loads of tiles t+1 and t+2 are in flight.  Tile t+1 is
+  // written to the other LDS buffers at the end of tile t (one barrier per
+  // tile); the set it came from is then reloaded with tile t+3.
+  Stage<EB> sa, sb;
+  load_stage(t0, sa);
+  store_stage(0, sa);
+  if (t0 + 1 < t1) load_stage(t0 + 1, sa);
+  if (t0 + 2 < t1) load_stage(t0 + 2, sb);
   __syncthreads();
 
-  const h16x2 ones = {(__fp16)1.0f, (__fp16)1.0f};
-
-  for (int64_t t = t0; t < t1; ++t) {
-    const int cur = (int)((t - t0) & 1);
-    const unsigned char* kb = kbuf[cur];
-    const unsigned char* vb = vbuf[cur];
-
-    // ---- S^T = K Q^T, two 32-key chunks
-    f32x16 s[QG][2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-#pragma unroll
-      for (int g = 0; g < QG; ++g) s[g][c] = O::qk(kb + (32 * c + col) * O::KROW, hf, qf[g]);
-    }
-
-    // ---- online softmax (base 2)
-    const bool last = (t + 1) * 64 > a.n;
-    f16x8 p16[QG][2][2];
-#pragma unroll
-    for (int g = 0; g < QG; ++g) {
-      if (last) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int64_t key = t * 64 + 32 * c + 16 * (r >> 3) + 8 * hf + (r & 7);
-            if (key >= a.n) s[g][c][r] = -INFINITY;
-          }
-      }
-      float mx = s[g][0][0];
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[g][c][r]);
-      float lo, hi;
-      halves(mx, lo, hi);
-      const float mcand = fmaxf(lo, hi) * c_scale;
-      const bool move = mcand > m_run[g] + kRescaleThreshold;
-      if (__builtin_amdgcn_ballot_w64(move) != 0) {  // wave-uniform branch
-        const float mnew = move ? mcand : m_run[g];
-        const float alpha = __builtin_amdgcn_exp2f(m_run[g] - mnew);  // exactly 1 when unmoved
-        m_run[g] = mnew;
-        l_run[g] *= alpha;
-        o[g][0] *= alpha;
-        o[g][1] *= alpha;
-      }
-      const float neg_m = -m_run[g];
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            p16[g][c][ks][e] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[g][c][8 * ks + e], c_scale, neg_m));
-      // l from the same rounded P: each packed 32-bit word of P is one
-      // fp16 pair, summed into fp32 by v_dot2 with (1, 1)
-      float lsum = l_run[g];
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const f16x8 pv = p16[g][c][ks];
-          const i32x4 words = __builtin_bit_cast(i32x4, pv);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // copy the element first: bit-casting a vector element directly
-            // reads element 0 with this compiler
-            const int word = words[i];
-            lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, word), ones, lsum, false);
-          }
-        }
-      l_run[g] = lsum;
-    }
-
-    // ---- O^T += V^T P^T
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-          const f16x8 va = *reinterpret_cast<const f16x8*>(vb + (32 * dt + col) * kVRow +
-                                                           (32 * c + 16 * ks + 8 * hf) * 2);
-#pragma unroll
-          for (int g = 0; g < QG; ++g)
-            o[g][dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, p16[g][c][ks], o[g][dt], 0, 0, 0);
-        }
-
-    // ---- stage the next tile (its loads were issued one iteration ago)
+  auto advance = [&](int64_t t, Stage<EB>& next) {
     if (t + 1 < t1) {
-      store_stage(cur ^ 1, st);
-      if (t + 2 < t1) load_stage(t + 2, st);
+      store_stage((int)((t + 1 - t0) & 1), next);
+      if (t + 3 < t1) load_stage(t + 3, next);
     }
     __syncthreads();
+  };
+  // tiles [t0, t_full) hold only valid keys; a partial tile can only be the
+  // context's last one
+  const int64_t t_full = (t1 * 64 > a.n) ? t1 - 1 : t1;
+  const int rem_last = (int)(a.n - (t1 - 1) * 64);
+  if (t0 < t_full)
+    attend_tile<PREC, QG, true, false>(ws, kbuf[0], vbuf[0], c_scale, col, hf, 64);
+  else
+    attend_tile<PREC, QG, true, true>(ws, kbuf[0], vbuf[0], c_scale, col, hf, rem_last);
+  advance(t0, sa);
+  // tile t0+1+2i takes its successor from sb, tile t0+2+2i from sa
+  int64_t t = t0 + 1;
+  for (; t + 1 < t_full; t += 2) {
+    attend_tile<PREC, QG, false, false>(ws, kbuf[1], vbuf[1], c_scale, col, hf, 64);
+    advance(t, sb);
+    attend_tile<PREC, QG, false, false>(ws, kbuf[0], vbuf[0], c_scale, col, hf, 64);
+    advance(t + 1, sa);
+  }
+  if (t < t_full) {
+    attend_tile<PREC, QG, false, false>(ws, kbuf[1], vbuf[1], c_scale, col, hf, 64);
+    advance(t, sb);
+    ++t;
+  }
+  if (t_full > t0 && t_full < t1) {
+    const int cur = (int)((t_full - t0) & 1);
+    attend_tile<PREC, QG, false, true>(ws, kbuf[cur], vbuf[cur], c_scale, col, hf, rem_last);
   }
 
   // ---- epilogue
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
     float lo, hi;
-    halves(l_run[g], lo, hi);
+    halves(ws.l_run[g], lo, hi);
     const float l_tot = lo + hi;
     const int64_t q = wq0 + g * 32 + col;
     if constexpr (SPLIT) {
       if (q < a.q_rows_valid) {
         const int64_t slot = ((int64_t)bh * a.q_rows_valid + q) * a.splits + split;
-        if (hf == 0) *reinterpret_cast<float2*>(a.part_ml + slot * 2) = float2{m_run[g], l_tot};
+        if (hf == 0) *reinterpret_cast<float2*>(a.part_ml + slot * 2) = make_float2(ws.m_run[g], l_tot);
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
-            const f32x4 v4 = {o[g][dt][4 * p], o[g][dt][4 * p + 1], o[g][dt][4 * p + 2], o[g][dt][4 * p + 3]};
+            const f32x4 v4 = {ws.o[g][dt][4 * p], ws.o[g][dt][4 * p + 1], ws.o[g][dt][4 * p + 2],
+                              ws.o[g][dt][4 * p + 3]};
             *reinterpret_cast<f32x4*>(a.part_o + slot * 64 + 32 * dt + 8 * p + 4 * hf) = v4;
           }
       }
@@ -344,7 +404,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
           for (int p = 0; p < 4; ++p) {
             f16x4 v4;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v4[e] = valid ? (_Float16)(o[g][dt][4 * p + e] * f) : (_Float16)0.0f;
+            for (int e = 0; e < 4; ++e) v4[e] = valid ? (_Float16)(ws.o[g][dt][4 * p + e] * f) : (_Float16)0.0f;
             *reinterpret_cast<f16x4*>(orow + 32 * dt + 8 * p + 4 * hf) = v4;
           }
       }
@@ -352,7 +412,25 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
   }
 }
 
-// One wavefront per (b, h, row); lane = head-dim element.  Fixed split order.
+// Full sums across a wavefront in a fixed butterfly order (every lane ends
+// with the same bits).
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// One wavefront per (b, h, row).  Splits are taken 64 at a time with lane s
+// owning split s for the maximum, the weights w_s = exp2(m_s - M) and the
+// weighted l; the head-dim accumulation then runs over the splits in order
+// with lane = head-dim element and the (uniform) weight read from lane s.
+// The order of every sum is fixed, so a row's result does not depend on the
+// launch or on the other rows.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
                                                       const float* __restrict__ s_v, int B, int H,
@@ -366,12 +444,26 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const float* ml = part_ml + item * splits * 2;
   const float* po = part_o + item * splits * 64;
   float m = -INFINITY;
-  for (int s = 0; s < splits; ++s) m = fmaxf(m, ml[2 * s]);
+  for (int s0 = 0; s0 < splits; s0 += 64)
+    if (s0 + lane < splits) m = fmaxf(m, ml[2 * (s0 + lane)]);
+  m = wave_max(m);
   float l = 0.f, acc = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float wgt = __builtin_amdgcn_exp2f(ml[2 * s] - m);
-    l = __builtin_fmaf(wgt, ml[2 * s + 1], l);
-    acc = __builtin_fmaf(wgt, po[s * 64 + lane], acc);
+  for (int s0 = 0; s0 < splits; s0 += 64) {
+    const int sl = s0 + lane;
+    const float wl = sl < splits ? __builtin_amdgcn_exp2f(ml[2 * sl] - m) : 0.f;
+    l += wave_sum(sl < splits ? wl * ml[2 * sl + 1] : 0.f);
+    const int cnt = splits - s0 < 64 ? splits - s0 : 64;
+    const float* pos = po + (int64_t)s0 * 64 + lane;
+    int s = 0;
+    for (; s + 4 <= cnt; s += 4) {
+      const float o0 = pos[(s + 0) * 64], o1 = pos[(s + 1) * 64];
+      const float o2 = pos[(s + 2) * 64], o3 = pos[(s + 3) * 64];
+      acc = __builtin_fmaf(__shfl(wl, s + 0, 64), o0, acc);
+      acc = __builtin_fmaf(__shfl(wl, s + 1, 64), o1, acc);
+      acc = __builtin_fmaf(__shfl(wl, s + 2, 64), o2, acc);
+      acc = __builtin_fmaf(__shfl(wl, s + 3, 64), o3, acc);
+    }
+    for (; s < cnt; ++s) acc = __builtin_fmaf(__shfl(wl, s, 64), pos[s * 64], acc);
   }
   const float sv = fp8 ? s_v[bh] : 1.0f;
   const _Float16 y = (_Float16)(acc * (sv / l));

@@ -42,7 +42,9 @@ namespace {
 
 constexpr uint64_t kMagic = 0x5344'4D49'434C'4131ull;  // "SDMICLA1"
 constexpr int64_t kFp8MinRows = 8192;
-constexpr int kTargetSplitsPerCu = 4;  // splits = num_cus / 4 (64 on 256 CUs)
+// KV splits per cache: 3/8 of the CU count (96 on 256 CUs), i.e. three
+// 4-wave workgroups per CU for every head of a 128-row query batch.
+constexpr int kSplitsPer8Cus = 3;
 constexpr int64_t kMinTilesPerSplit = 4;
 
 thread_local std::string g_error;
@@ -105,7 +107,7 @@ int32_t resolve_precision(int64_t n, int32_t requested) {
 
 void plan_splits(int64_t n, int32_t num_cus, int32_t* splits, int64_t* tiles_per_split) {
   const int64_t tiles = (n + kKeyTile - 1) / kKeyTile;
-  int64_t target = num_cus / kTargetSplitsPerCu;
+  int64_t target = (int64_t)num_cus * kSplitsPer8Cus / 8;
   if (target < 1) target = 1;
   int64_t tps = (tiles + target - 1) / target;
   if (tps < kMinTilesPerSplit) tps = kMinTilesPerSplit;

@@ -70,7 +70,7 @@ def test_split_plan_is_a_function_of_n_only():
         s, kps = B.sdm_icl_split_plan(n, 256)
         assert kps % 64 == 0 and s >= 1
         assert (s - 1) * kps < n <= s * kps   # every split holds at least one valid key
-    assert B.sdm_icl_split_plan(524288, 256) == (64, 8192)
+    assert B.sdm_icl_split_plan(524288, 256) == (96, 5504)
     with pytest.raises(B.SdmIclError):
         B.sdm_icl_split_plan(0, 256)
 
