@@ -45,18 +45,23 @@ def kernel_source_hash() -> str:
 
 
 def counter_traffic(kernel: str):
-    """HBM bytes per launch measured with rocprofv3 counters for this exact
-    kernel source, or None if no measurement matches the current source."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    """HBM bytes per launch measured with rocprofv3 FETCH_SIZE / WRITE_SIZE
+    counters (calibrated against a plain copy) for this exact kernel source,
+    or None if no measurement matches the current source."""
+    path = os.path.join(ROOT, "profiles", "traffic_context_model512k.txt")
+    rec = {}
     try:
         with open(path) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    rec[k.strip()] = v.strip()
+    except OSError:
         return None
     if rec.get("source_hash") != kernel_source_hash():
         return None
-    k = rec.get("kernels", {}).get(kernel)
-    return None if k is None else k.get("bytes_per_launch")
+    v = rec.get(f"{kernel}.bytes_per_launch")
+    return None if v is None else int(float(v))
 
 
 def dev(a):
@@ -192,6 +197,8 @@ def main() -> int:
     ap.add_argument("--cached-reps", type=int, default=30)
     ap.add_argument("--no-cached", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-model-call", action="store_true",
+                    help="skip the model-call measurement (only the cached-prediction leg runs)")
     ap.add_argument("--cpu-sample-rows", type=int, default=32)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times) and exit; "
@@ -221,6 +228,12 @@ def main() -> int:
         return 0
     B.lib()
 
+    if args.no_model_call:
+        wc = gen.WORKLOADS[args.cached_workload]
+        cres, cinfo = bench_cached(B, gen, wc, args.cached_reps)
+        print(json.dumps({"cached": {"workload": wc.name, "kv_splits": cinfo["kv_splits"],
+                                     "batches": {str(k): v for k, v in cres.items()}}}), flush=True)
+        return 0
     w = gen.WORKLOADS[args.workload]
     log(f"[bench] model call {w.name}: n_pad={w.n_pad} n={w.n_valid} R={w.n_query} H={w.heads}")
     x, info, sec, t = bench_model_call(B, gen, w, args.steps, args.warmup)

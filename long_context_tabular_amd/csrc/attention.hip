@@ -140,80 +140,91 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
   return fmaxf(lo, hi);
 }
 
-// P = fp16(exp2(s * c - m)) for the lane's 32 scores; returns the fp32 sum of
-// the rounded P (v_dot2 of each packed fp16 pair with (1, 1)).
-__device__ __forceinline__ float exp_tile(const f32x16 (&s)[2], float c_scale, float neg_m,
-                                          f16x8 (&p16)[2][2]) {
+// P = fp16(exp2(s * c - m)) for the lane's 16 scores of one 32-key chunk;
+// returns the fp32 sum of the rounded P (v_dot2 of each packed fp16 pair
+// with (1, 1)).
+__device__ __forceinline__ float exp_chunk(const f32x16& s, float c_scale, float neg_m,
+                                           f16x8 (&p16)[2]) {
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        p16[c][ks][e] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[c][8 * ks + e], c_scale, neg_m));
+    for (int e = 0; e < 8; ++e)
+      p16[ks][e] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * ks + e], c_scale, neg_m));
   const h16x2 ones = {(__fp16)1.0f, (__fp16)1.0f};
   float lsum = 0.f;
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int ks = 0; ks < 2; ++ks) {
+    const f16x8 pv = p16[ks];
+    const i32x4 words = __builtin_bit_cast(i32x4, pv);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const f16x8 pv = p16[c][ks];
-      const i32x4 words = __builtin_bit_cast(i32x4, pv);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // copy the element first: bit-casting a vector element directly
-        // reads element 0 with this compiler
-        const int word = words[i];
-        lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, word), ones, lsum, false);
-      }
+    for (int i = 0; i < 4; ++i) {
+      // copy the element first: bit-casting a vector element directly
+      // reads element 0 with this compiler
+      const int word = words[i];
+      lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, word), ones, lsum, false);
     }
+  }
   return lsum;
+}
+
+// Scores of one 32-key chunk with keys >= n set to -inf (MASK only).
+template <int PREC, bool MASK>
+__device__ __forceinline__ f32x16 chunk_scores(const unsigned char* kb, int c, int col, int hf,
+                                               const typename Ops<PREC>::QFrag& q, int rem) {
+  f32x16 sc = Ops<PREC>::qk(kb + (32 * c + col) * Ops<PREC>::KROW, hf, q);
+  if constexpr (MASK) {
+    const int lim = rem - 8 * hf;  // key offset in the tile = 32c + 16(r/8) + 8hf + r%8
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (32 * c + 16 * (r >> 3) + (r & 7) >= lim) sc[r] = -INFINITY;
+  }
+  return sc;
 }
 
 // One 64-key tile for all QG groups of the wave.  FIRST: the first tile of
 // the wave's KV range, which sets the reference maximum.  MASK: the tile holds
 // keys >= n (only the last tile of the context can), 'rem' = n - tile start.
+// Each 32-key chunk's scores are turned into P as soon as its MFMA returns,
+// so only one chunk of scores is live; the rare overflow path recomputes
+// the scores instead of keeping them.
 template <int PREC, int QG, bool FIRST, bool MASK>
 __device__ __forceinline__ void attend_tile(WaveState<PREC, QG>& w, const unsigned char* kb,
                                             const unsigned char* vb, float c_scale, int col,
                                             int hf, int rem) {
-  typedef Ops<PREC> O;
-  // ---- S^T = K Q^T, two 32-key chunks
-  f32x16 s[QG][2];
-#pragma unroll
-  for (int c = 0; c < 2; ++c)
-#pragma unroll
-    for (int g = 0; g < QG; ++g) s[g][c] = O::qk(kb + (32 * c + col) * O::KROW, hf, w.qf[g]);
-
-  // ---- softmax weights (base 2)
   f16x8 p16[QG][2][2];
 #pragma unroll
   for (int g = 0; g < QG; ++g) {
-    if constexpr (MASK) {
-      const int lim = rem - 8 * hf;  // key offset in the tile = 32c + 16(r/8) + 8hf + r%8
+    float lt;
+    if constexpr (FIRST) {
+      f32x16 s[2];
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int c = 0; c < 2; ++c) s[c] = chunk_scores<PREC, MASK>(kb, c, col, hf, w.qf[g], rem);
+      w.m_run[g] = tile_max(s) * c_scale;
+      lt = exp_chunk(s[0], c_scale, -w.m_run[g], p16[g][0]) + exp_chunk(s[1], c_scale, -w.m_run[g], p16[g][1]);
+    } else {
+      lt = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * c + 16 * (r >> 3) + (r & 7) >= lim) s[g][c][r] = -INFINITY;
-    }
-    if constexpr (FIRST) w.m_run[g] = tile_max(s[g]) * c_scale;
-    float lt = exp_tile(s[g], c_scale, -w.m_run[g], p16[g]);
-    if constexpr (!FIRST) {
+      for (int c = 0; c < 2; ++c) {
+        const f32x16 sc = chunk_scores<PREC, MASK>(kb, c, col, hf, w.qf[g], rem);
+        lt += exp_chunk(sc, c_scale, -w.m_run[g], p16[g][c]);
+      }
       float lo, hi;
       halves(lt, lo, hi);
       const bool over = !(lo + hi <= kMaxTileSum);  // also true for inf
       if (__builtin_amdgcn_ballot_w64(over) != 0) {  // rare, wave-uniform
         // only rows that overflowed move their reference (others keep it
         // bit for bit, so a row never depends on its neighbours)
-        const float mt = tile_max(s[g]) * c_scale;
+        f32x16 s[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) s[c] = chunk_scores<PREC, MASK>(kb, c, col, hf, w.qf[g], rem);
+        const float mt = tile_max(s) * c_scale;
         const float mnew = over ? fmaxf(w.m_run[g], mt) : w.m_run[g];
         const float alpha = __builtin_amdgcn_exp2f(w.m_run[g] - mnew);
         w.m_run[g] = mnew;
         w.l_run[g] *= alpha;
         w.o[g][0] *= alpha;
         w.o[g][1] *= alpha;
-        lt = exp_tile(s[g], c_scale, -mnew, p16[g]);
+        lt = exp_chunk(s[0], c_scale, -mnew, p16[g][0]) + exp_chunk(s[1], c_scale, -mnew, p16[g][1]);
       }
     }
     w.l_run[g] += lt;
