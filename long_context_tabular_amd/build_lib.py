@@ -19,6 +19,9 @@ CSRC = os.path.join(PKG, "csrc")
 LIB_NAME = "libsdm_icl_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["prep.hip", "attention.hip", "sdm_icl_attn.cpp"]
+# per-source flags: the attention kernels schedule for instruction-level
+# parallelism (measured ~5% faster on the 512K context pass)
+EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-ffp-contract=off",
@@ -50,7 +53,8 @@ def build(verbose: bool = False, save_temps_dir: str | None = None) -> str:
                 os.makedirs(save_temps_dir, exist_ok=True)
                 obj = os.path.join(save_temps_dir, src + ".o")
                 extra = ["-save-temps=obj"]
-            _run([HIPCC, *COMMON, *extra, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+            _run([HIPCC, *COMMON, *EXTRA.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj],
+                 verbose)
             objs.append(obj)
         out_tmp = LIB_PATH + ".tmp"
         _run([HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", out_tmp], verbose)

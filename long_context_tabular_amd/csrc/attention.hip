@@ -24,8 +24,10 @@
 //   * Online softmax in base 2 (the scale is folded into one FMA per score).
 //     The first tile of a wave's KV range sets each row's reference maximum;
 //     later tiles compute P against it with no per-tile max at all, and a row
-//     moves its reference (rescaling O and l) only when its 64 rounded P of a
-//     tile sum to more than 2^14, which bounds every P below fp16's range.
+//     moves its reference (rescaling O and l) only when the 32 rounded P one
+//     of its lanes holds in a tile sum to more than 2^13, which bounds every
+//     P below fp16's range; the check is per lane, with one wave-uniform
+//     branch per tile.
 //     Full tiles carry no masking code; the ragged last tile of the context
 //     is a separate instantiation.
 //   * O^T += V^T P^T with v_mfma_f32_32x32x16_f16; P is rounded to fp16
@@ -53,9 +55,10 @@ typedef __fp16 h16x2 __attribute__((ext_vector_type(2)));
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 // After a row's first tile, P is taken against a reference maximum that is
-// moved only when a tile's 64 rounded P values of that row sum to more than
-// this; every P then stays <= 2^14 (finite in fp16) without a per-tile max.
-constexpr float kMaxTileSum = 16384.0f;
+// moved only when the 32 rounded P values one lane holds for that row in a
+// tile sum to more than this; every P then stays <= 2^13 (finite in fp16)
+// without a per-tile max.
+constexpr float kMaxLaneSum = 8192.0f;
 
 // Row r of a 32-row MFMA A operand holds key sigma(r) of its 32-key chunk:
 // bits 2 and 3 of r swapped.  With the 32x32 output layout (lane l, register
@@ -192,28 +195,43 @@ __device__ __forceinline__ void attend_tile(WaveState<PREC, QG>& w, const unsign
                                             const unsigned char* vb, float c_scale, int col,
                                             int hf, int rem) {
   f16x8 p16[QG][2][2];
+  if constexpr (FIRST) {
 #pragma unroll
-  for (int g = 0; g < QG; ++g) {
-    float lt;
-    if constexpr (FIRST) {
+    for (int g = 0; g < QG; ++g) {
       f32x16 s[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) s[c] = chunk_scores<PREC, MASK>(kb, c, col, hf, w.qf[g], rem);
       w.m_run[g] = tile_max(s) * c_scale;
-      lt = exp_chunk(s[0], c_scale, -w.m_run[g], p16[g][0]) + exp_chunk(s[1], c_scale, -w.m_run[g], p16[g][1]);
-    } else {
-      lt = 0.f;
+      w.l_run[g] = exp_chunk(s[0], c_scale, -w.m_run[g], p16[g][0]) +
+                   exp_chunk(s[1], c_scale, -w.m_run[g], p16[g][1]);
+    }
+  } else {
+    // each lane checks that its own 32 rounded P of each group sum to at most
+    // kMaxLaneSum, which bounds every P it holds; one wave-uniform branch per
+    // tile covers all groups
+    float lt[QG];
+    bool ok = true;
+#pragma unroll
+    for (int g = 0; g < QG; ++g) {
+      lt[g] = 0.f;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const f32x16 sc = chunk_scores<PREC, MASK>(kb, c, col, hf, w.qf[g], rem);
-        lt += exp_chunk(sc, c_scale, -w.m_run[g], p16[g][c]);
+        lt[g] += exp_chunk(sc, c_scale, -w.m_run[g], p16[g][c]);
       }
-      float lo, hi;
-      halves(lt, lo, hi);
-      const bool over = !(lo + hi <= kMaxTileSum);  // also true for inf
-      if (__builtin_amdgcn_ballot_w64(over) != 0) {  // rare, wave-uniform
-        // only rows that overflowed move their reference (others keep it
-        // bit for bit, so a row never depends on its neighbours)
+      ok = ok && (lt[g] <= kMaxLaneSum);  // false for inf
+    }
+    if (__builtin_amdgcn_ballot_w64(!ok) != 0) {  // rare, wave-uniform
+      // A row moves its reference only if one of its two lanes overflowed;
+      // both lanes of a row take the same decision, and rows that did not
+      // overflow keep their reference bit for bit (a row never depends on its
+      // neighbours).
+#pragma unroll
+      for (int g = 0; g < QG; ++g) {
+        float lo, hi;
+        halves(lt[g], lo, hi);
+        const bool over = !(lo <= kMaxLaneSum && hi <= kMaxLaneSum);
+        if (__builtin_amdgcn_ballot_w64(over) == 0) continue;
         f32x16 s[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c) s[c] = chunk_scores<PREC, MASK>(kb, c, col, hf, w.qf[g], rem);
@@ -224,10 +242,11 @@ __device__ __forceinline__ void attend_tile(WaveState<PREC, QG>& w, const unsign
         w.l_run[g] *= alpha;
         w.o[g][0] *= alpha;
         w.o[g][1] *= alpha;
-        lt = exp_chunk(s[0], c_scale, -mnew, p16[g][0]) + exp_chunk(s[1], c_scale, -mnew, p16[g][1]);
+        lt[g] = exp_chunk(s[0], c_scale, -mnew, p16[g][0]) + exp_chunk(s[1], c_scale, -mnew, p16[g][1]);
       }
     }
-    w.l_run[g] += lt;
+#pragma unroll
+    for (int g = 0; g < QG; ++g) w.l_run[g] += lt[g];
   }
 
   // ---- O^T += V^T P^T
@@ -495,8 +514,7 @@ hipError_t launch_attention(const AttnArgs& a, int prec, bool split, hipStream_t
     if (wide) { if (split) SDM_ATT(kPrecFp8, 2, true); else SDM_ATT(kPrecFp8, 2, false); }
     else { if (split) SDM_ATT(kPrecFp8, 1, true); else SDM_ATT(kPrecFp8, 1, false); }
   } else {
-    if (wide) { if (split) SDM_ATT(kPrecFp16, 2, true); else SDM_ATT(kPrecFp16, 2, false); }
-    else { if (split) SDM_ATT(kPrecFp16, 1, true); else SDM_ATT(kPrecFp16, 1, false); }
+    if (split) SDM_ATT(kPrecFp16, 1, true); else SDM_ATT(kPrecFp16, 1, false);
   }
 #undef SDM_ATT
   return hipGetLastError();

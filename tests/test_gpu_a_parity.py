@@ -250,3 +250,37 @@ def test_auto_precision_follows_threshold():
         c = B.sdm_icl_attn_fit(r.q, r.k, r.v, n, precision=B.SDM_ICL_PREC_AUTO)
         assert c.info()["precision"] == want
         c.release()
+
+
+@pytest.mark.parametrize("prec", [B.SDM_ICL_PREC_FP16, B.SDM_ICL_PREC_FP8_E4M3])
+def test_reference_moves_when_later_tiles_dominate(prec):
+    """Keys whose scale grows along the context make later tiles' scores
+    exceed a row's first-tile reference by far, so the reference-moving path
+    runs many times; near-zero queries (every other row) never trigger it.
+    Parity with the oracle, and bitwise batch-split invariance for rows whose
+    neighbours take that path."""
+    torch = _torch()
+    rng = np.random.default_rng(21)
+    N, H, R = 2048, 2, 64
+    growth = (1.0 + np.arange(N) / 35.0)[None, :, None, None]
+    q = (rng.standard_normal((1, N, H, 64))).astype(np.float16)
+    k = (rng.standard_normal((1, N, H, 64)) * growth / 8).astype(np.float16)
+    v = (rng.standard_normal((1, N, H, 64)) / 8).astype(np.float16)
+    qq = (rng.standard_normal((1, R, H, 64))).astype(np.float16)
+    q[:, 1::2] *= np.float16(1e-3)
+    qq[:, 1::2] *= np.float16(1e-3)
+    say("reference moves", prec)
+    out = torch.empty((1, N, H, 64), dtype=torch.float16, device="cuda")
+    c = B.sdm_icl_attn_fit(to_dev(q), to_dev(k), to_dev(v), N, precision=prec, out_ctx=out)
+    full = B.sdm_icl_attn_query(c, to_dev(qq)).cpu().numpy()
+    halves_ = np.concatenate([B.sdm_icl_attn_query(c, to_dev(qq[:, :32])).cpu().numpy(),
+                              B.sdm_icl_attn_query(c, to_dev(qq[:, 32:])).cpu().numpy()], axis=1)
+    torch.cuda.synchronize()
+    c.release()
+    np.testing.assert_array_equal(full.view(np.uint16), halves_.view(np.uint16))
+    ref = icl.fit(q, k, v, N, icl.SCALE_NONE, prec)
+    rows = np.concatenate([np.arange(0, 64), np.arange(N - 64, N)])
+    e_c = norm_err(out.cpu().numpy()[0, rows].astype(np.float64), icl.context_outputs(ref, q, None, rows))
+    e_q = norm_err(full[0].astype(np.float64), icl.attend(ref, qq[0], None))
+    say(f"  context err {e_c:.3e} query err {e_q:.3e}")
+    assert e_c <= TOL[prec] and e_q <= TOL[prec]
