@@ -123,34 +123,57 @@ def bench_cached(B, gen, w, reps):
     qq = dev(x.q_query)
     gq = dev(x.gate_query) if gated else None
     res = {}
+    n, H, D = w.n_valid, w.heads, w.head_dim
     for R in w.query_batches:
         ws = torch.empty(B.sdm_icl_attn_query_workspace_size(cache, R), dtype=torch.uint8, device="cuda")
-        qb = qq[:, :R].contiguous()
-        gb = gq[:, :R].contiguous() if gq is not None else None
-        ob = torch.empty_like(qb)
+        nb = max(1, w.n_query // R)                 # batches that cover the query set once
+        qbs = [qq[:, i * R:(i + 1) * R].contiguous() for i in range(nb)]
+        gbs = [gq[:, i * R:(i + 1) * R].contiguous() if gq is not None else None for i in range(nb)]
+        obs = [torch.empty_like(qb) for qb in qbs]
         for _ in range(10):
-            B.sdm_icl_attn_query(cache, qb, gb, out=ob, workspace=ws)
+            B.sdm_icl_attn_query(cache, qbs[0], gbs[0], out=obs[0], workspace=ws)
         torch.cuda.synchronize()
-        B.sdm_icl_timing_enable(True)
-        for cls in range(5):
-            B.sdm_icl_timing_read(cls)
+        # (1) one call at a time: the latency a single predict batch sees
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         for a, b in evs:
             a.record()
-            B.sdm_icl_attn_query(cache, qb, gb, out=ob, workspace=ws)
+            B.sdm_icl_attn_query(cache, qbs[0], gbs[0], out=obs[0], workspace=ws)
             b.record()
         torch.cuda.synchronize()
-        kq_ms, kq_n = B.sdm_icl_timing_read(B.SDM_ICL_TIMING_QUERY)
-        B.sdm_icl_timing_enable(False)
         times = sorted(a.elapsed_time(b) for a, b in evs)
         med = times[len(times) // 2]
-        n, H, D = w.n_valid, w.heads, w.head_dim
+        # (2) the whole query set as nb batches of R rows issued back to back
+        greps = max(3, reps // nb)
+        gevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(greps)]
+        for a, b in gevs:
+            a.record()
+            for qb, gb, ob in zip(qbs, gbs, obs):
+                B.sdm_icl_attn_query(cache, qb, gb, out=ob, workspace=ws)
+            b.record()
+        torch.cuda.synchronize()
+        gtimes = sorted(a.elapsed_time(b) for a, b in gevs)
+        gmed = gtimes[len(gtimes) // 2] / nb
+        # (3) per-kernel durations (library events around each launch)
+        B.sdm_icl_timing_enable(True)
+        for cls in range(5):
+            B.sdm_icl_timing_read(cls)
+        for _ in range(reps):
+            B.sdm_icl_attn_query(cache, qbs[0], gbs[0], out=obs[0], workspace=ws)
+        torch.cuda.synchronize()
+        kt = {name: B.sdm_icl_timing_read(cls) for name, cls in
+              (("scale", B.SDM_ICL_TIMING_SCALE), ("attention", B.SDM_ICL_TIMING_QUERY),
+               ("combine", B.SDM_ICL_TIMING_COMBINE))}
+        B.sdm_icl_timing_enable(False)
+        kus = {k: ms / max(cnt, 1) * 1e3 for k, (ms, cnt) in kt.items()}
         alg_bytes = 2 * n * H * D + R * H * D * 2 * 2 + (R * H * 2 if gated else 0)
         flops = 4.0 * R * n * D * H
         res[R] = {"us_median": med * 1e3, "us_min": times[0] * 1e3, "us_max": times[-1] * 1e3,
                   "GB_per_s": alg_bytes / (med * 1e-3) / 1e9, "TFLOP_per_s": flops / (med * 1e-3) / 1e12,
-                  "attention_kernel_us": kq_ms / max(kq_n, 1) * 1e3,
-                  "attention_kernel_GB_per_s": alg_bytes / (kq_ms / max(kq_n, 1) * 1e-3) / 1e9,
+                  "batches_in_sequence": nb, "us_per_batch_in_sequence": gmed * 1e3,
+                  "GB_per_s_in_sequence": alg_bytes / (gmed * 1e-3) / 1e9,
+                  "kernel_us": kus,
+                  "attention_kernel_us": kus["attention"],
+                  "attention_kernel_GB_per_s": alg_bytes / (kus["attention"] * 1e-6) / 1e9,
                   "algorithmic_bytes": alg_bytes}
     info = cache.info()
     cache.release()

@@ -33,6 +33,10 @@
  * ------------------------------
  * - Pointers named "device" are HIP device memory on the stream's device and
  *   stay owned by the caller; "host" pointers are read during the call only.
+ * - Device fp16 row tensors (q, k, v, outputs) and the query workspace must be
+ *   16-byte aligned (the kernels move them 16 bytes at a time), gates 2-byte
+ *   and float arrays 4-byte aligned; a misaligned pointer is
+ *   SDM_ICL_E_INVALID, found before anything touches the device.
  * - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *   All device work is enqueued on it; no entry point synchronises the host
  *   unless stated (cache_export does).
@@ -195,9 +199,11 @@ sdm_icl_status sdm_icl_head_factors(int64_t n, const float* head_coef, int32_t h
 /* Precision a fit with this n and request resolves to (AUTO: FP8 iff n > 8192). */
 int32_t sdm_icl_select_precision(int64_t n, int32_t requested);
 
-/* KV split plan for n valid keys on a device with num_cus compute units:
- * a pure function of (n, num_cus), never of the query count. */
-sdm_icl_status sdm_icl_split_plan(int64_t n, int32_t num_cus, int32_t* kv_splits,
+/* KV split plan for n valid keys and bh_count = batch * heads on a device with
+ * num_cus compute units: about 4 * num_cus / bh_count splits of at least 4
+ * key tiles each.  A pure function of (n, num_cus, bh_count), never of the
+ * query count, so every query batch of a cache uses the same plan. */
+sdm_icl_status sdm_icl_split_plan(int64_t n, int32_t num_cus, int32_t bh_count, int32_t* kv_splits,
                                   int64_t* keys_per_split);
 
 /* Message of the last non-OK status on this thread ("" if none). */

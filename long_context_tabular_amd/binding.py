@@ -74,7 +74,7 @@ _SIGNATURES = {
     "sdm_icl_head_factors": (ctypes.c_int32, [ctypes.c_int64, ctypes.POINTER(ctypes.c_float),
                                               ctypes.c_int32, ctypes.POINTER(ctypes.c_uint16)]),
     "sdm_icl_select_precision": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32]),
-    "sdm_icl_split_plan": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32,
+    "sdm_icl_split_plan": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]),
     "sdm_icl_last_error": (ctypes.c_char_p, []),
     "sdm_icl_version": (ctypes.c_int32, []),
@@ -148,10 +148,11 @@ def sdm_icl_select_precision(n: int, requested: int) -> int:
     return lib().sdm_icl_select_precision(int(n), int(requested))
 
 
-def sdm_icl_split_plan(n: int, num_cus: int):
+def sdm_icl_split_plan(n: int, num_cus: int, bh_count: int):
     s = ctypes.c_int32()
     k = ctypes.c_int64()
-    _check(lib().sdm_icl_split_plan(int(n), int(num_cus), ctypes.byref(s), ctypes.byref(k)))
+    _check(lib().sdm_icl_split_plan(int(n), int(num_cus), int(bh_count), ctypes.byref(s),
+                                    ctypes.byref(k)))
     return s.value, k.value
 
 

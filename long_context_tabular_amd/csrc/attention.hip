@@ -12,7 +12,9 @@
 // FP8 attention and caching into TabICLv2" (shared attention projects Q/K/V
 // and falls back to SDPA; FP8 Q/K/V with per-head scales).
 //
-// Data flow of one workgroup (4 wavefronts, each owning QG x 32 query rows):
+// Data flow of one workgroup (W = 2 or 4 wavefronts, each owning QG x 32
+// query rows; a wavefront walks its whole KV range, so the block shape does
+// not change any row's arithmetic):
 //   * Q stays in VGPRs for the whole KV loop (MFMA B operand).
 //   * 64-key tiles of K and of V are fetched as separate loads into registers
 //     two tiles ahead, and written into separate double-buffered LDS stages
@@ -52,8 +54,6 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef __fp16 h16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
 // After a row's first tile, P is taken against a reference maximum that is
 // moved only when the 32 rounded P values one lane holds for that row in a
 // tile sum to more than this; every P then stays <= 2^13 (finite in fp16)
@@ -118,10 +118,10 @@ struct Ops<kPrecFp16> {
 
 constexpr int kVRow = 144;  // LDS bytes per d-row of the fp16 V^T tile (128 + 16 pad)
 
-// Staging registers of one thread for one K tile and one V tile: 16 d of one
-// key (K, row-major) and 16 keys of one d (V, tile-transposed).
-template <int EB>
-struct Stage { i32x4 k[EB]; i32x4 v[EB]; };
+// Staging registers of one thread for one K tile and one V tile: R chunks of
+// 16 d of one key (K, row-major) and 16 keys of one d (V, tile-transposed).
+template <int EB, int R>
+struct Stage { i32x4 k[R][EB]; i32x4 v[R][EB]; };
 
 // Per-wave running state: Q fragments, reference maxima (log2 units), row
 // sums of P and the O^T accumulators of QG groups of 32 query rows.
@@ -264,11 +264,13 @@ __device__ __forceinline__ void attend_tile(WaveState<PREC, QG>& w, const unsign
       }
 }
 
-template <int PREC, int QG, bool SPLIT>
-__global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
+template <int PREC, int QG, bool SPLIT, int W>
+__global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
   typedef Ops<PREC> O;
   constexpr int EB = O::EB;
-  constexpr int QT = kWaves * QG * 32;
+  constexpr int NT = W * 64;      // threads per workgroup
+  constexpr int R = 256 / NT;     // 16-element staging chunks per thread and tile
+  constexpr int QT = W * QG * 32;
   constexpr int KTILE = 64 * O::KROW;
   constexpr int VTILE = 64 * kVRow;
   __shared__ __attribute__((aligned(16))) unsigned char kbuf[2][KTILE];
@@ -285,7 +287,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
     if constexpr (!SPLIT) {
       // rows past the valid context: zeros (16 bytes per thread per step)
       const int64_t r_end = a.out_rows < q0 + QT ? a.out_rows : q0 + QT;
-      for (int64_t i = tid; i < (r_end - q0) * 8; i += kThreads) {
+      for (int64_t i = tid; i < (r_end - q0) * 8; i += NT) {
         const int64_t r = q0 + i / 8;
         reinterpret_cast<i32x4*>(a.out)[((int64_t)b * a.out_rows + r) * a.heads * 8 + h * 8 + (i & 7)] =
             i32x4{0, 0, 0, 0};
@@ -321,40 +323,53 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
   const unsigned char* kg = reinterpret_cast<const unsigned char*>(a.kc) + (int64_t)bh * a.n_alloc * 64 * EB;
   const unsigned char* vg = reinterpret_cast<const unsigned char*>(a.vt) + (int64_t)bh * a.n_alloc * 64 * EB;
 
-  // thread -> staging coordinates: K key kr = tid/4, d-quarter tid%4;
-  //                                 V d-row tid/4, key-quarter tid%4
-  const int sr = tid >> 2, sq = tid & 3;
-  const int k_lds = (32 * (sr >> 5) + sigma(sr & 31)) * O::KROW + sq * 16 * EB;
-  const int v_lds = sr * kVRow + sq * 32;
-
-  auto load_stage = [&](int64_t t, Stage<EB>& st) {
-    const i32x4* kp = reinterpret_cast<const i32x4*>(kg + t * 64 * 64 * EB + tid * 16 * EB);
-    const i32x4* vp = reinterpret_cast<const i32x4*>(vg + t * 64 * 64 * EB + tid * 16 * EB);
-#pragma unroll
-    for (int c = 0; c < EB; ++c) st.k[c] = kp[c];
-#pragma unroll
-    for (int c = 0; c < EB; ++c) st.v[c] = vp[c];
+  // staging chunk ci = tid + i * NT (256 per tile): K key ci/4, d-quarter ci%4;
+  //                                                V d-row ci/4, key-quarter ci%4
+  auto k_lds = [&](int i) {
+    const int ci = tid + i * NT, sr = ci >> 2, sq = ci & 3;
+    return (32 * (sr >> 5) + sigma(sr & 31)) * O::KROW + sq * 16 * EB;
   };
-  auto store_stage = [&](int buf, const Stage<EB>& st) {
+  auto v_lds = [&](int i) {
+    const int ci = tid + i * NT;
+    return (ci >> 2) * kVRow + (ci & 3) * 32;
+  };
+
+  auto load_stage = [&](int64_t t, Stage<EB, R>& st) {
 #pragma unroll
-    for (int c = 0; c < EB; ++c) *reinterpret_cast<i32x4*>(&kbuf[buf][k_lds + 16 * c]) = st.k[c];
-    if constexpr (PREC == kPrecFp8) {
-      // widen 16 e4m3 codes to fp16 (exact) once per workgroup
-      i32x4 lo, hi;
+    for (int i = 0; i < R; ++i) {
+      const int64_t off = t * 64 * 64 * EB + (int64_t)(tid + i * NT) * 16 * EB;
+      const i32x4* kp = reinterpret_cast<const i32x4*>(kg + off);
+      const i32x4* vp = reinterpret_cast<const i32x4*>(vg + off);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int word = st.v[0][e];
-        const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, false);
-        const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, true);
-        const int w0 = __builtin_bit_cast(int, p0), w1 = __builtin_bit_cast(int, p1);
-        if (e < 2) { lo[2 * e] = w0; lo[2 * e + 1] = w1; }
-        else { hi[2 * (e - 2)] = w0; hi[2 * (e - 2) + 1] = w1; }
+      for (int c = 0; c < EB; ++c) st.k[i][c] = kp[c];
+#pragma unroll
+      for (int c = 0; c < EB; ++c) st.v[i][c] = vp[c];
+    }
+  };
+  auto store_stage = [&](int buf, const Stage<EB, R>& st) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int kl = k_lds(i), vl = v_lds(i);
+#pragma unroll
+      for (int c = 0; c < EB; ++c) *reinterpret_cast<i32x4*>(&kbuf[buf][kl + 16 * c]) = st.k[i][c];
+      if constexpr (PREC == kPrecFp8) {
+        // widen 16 e4m3 codes to fp16 (exact) once per workgroup
+        i32x4 lo, hi;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int word = st.v[i][0][e];
+          const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, false);
+          const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(word, 1.0f, true);
+          const int w0 = __builtin_bit_cast(int, p0), w1 = __builtin_bit_cast(int, p1);
+          if (e < 2) { lo[2 * e] = w0; lo[2 * e + 1] = w1; }
+          else { hi[2 * (e - 2)] = w0; hi[2 * (e - 2) + 1] = w1; }
+        }
+        *reinterpret_cast<i32x4*>(&vbuf[buf][vl]) = lo;
+        *reinterpret_cast<i32x4*>(&vbuf[buf][vl + 16]) = hi;
+      } else {
+        *reinterpret_cast<i32x4*>(&vbuf[buf][vl]) = st.v[i][0];
+        *reinterpret_cast<i32x4*>(&vbuf[buf][vl + 16]) = st.v[i][1];
       }
-      *reinterpret_cast<i32x4*>(&vbuf[buf][v_lds]) = lo;
-      *reinterpret_cast<i32x4*>(&vbuf[buf][v_lds + 16]) = hi;
-    } else {
-      *reinterpret_cast<i32x4*>(&vbuf[buf][v_lds]) = st.v[0];
-      *reinterpret_cast<i32x4*>(&vbuf[buf][v_lds + 16]) = st.v[1];
     }
   };
 
@@ -362,14 +377,14 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
   // processed, the loads of tiles t+1 and t+2 are in flight.  Tile t+1 is
   // written to the other LDS buffers at the end of tile t (one barrier per
   // tile); the set it came from is then reloaded with tile t+3.
-  Stage<EB> sa, sb;
+  Stage<EB, R> sa, sb;
   load_stage(t0, sa);
   store_stage(0, sa);
   if (t0 + 1 < t1) load_stage(t0 + 1, sa);
   if (t0 + 2 < t1) load_stage(t0 + 2, sb);
   __syncthreads();
 
-  auto advance = [&](int64_t t, Stage<EB>& next) {
+  auto advance = [&](int64_t t, Stage<EB, R>& next) {
     if (t + 1 < t1) {
       store_stage((int)((t + 1 - t0) & 1), next);
       if (t + 3 < t1) load_stage(t + 3, next);
@@ -455,12 +470,14 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// One wavefront per (b, h, row).  Splits are taken 64 at a time with lane s
-// owning split s for the maximum, the weights w_s = exp2(m_s - M) and the
-// weighted l; the head-dim accumulation then runs over the splits in order
-// with lane = head-dim element and the (uniform) weight read from lane s.
-// The order of every sum is fixed, so a row's result does not depend on the
-// launch or on the other rows.
+// One wavefront per (b, h, row); splits are taken 64 at a time.  Lane s of
+// a chunk owns split s for the maximum M, the weight w_s = exp2(m_s - M) and
+// the weighted l.  For the head-dim sum, lane 16g + j owns d in [4j, 4j + 4)
+// and the splits s = g (mod 4) of the chunk: it issues all of their loads
+// first and then adds them in increasing s; the four partial sums are added
+// in a fixed butterfly order, (g0 + g1) + (g2 + g3).  The order of every sum
+// is fixed, so a row's result does not depend on the launch or on the other
+// rows.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
                                                       const float* __restrict__ s_v, int B, int H,
@@ -477,46 +494,70 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   for (int s0 = 0; s0 < splits; s0 += 64)
     if (s0 + lane < splits) m = fmaxf(m, ml[2 * (s0 + lane)]);
   m = wave_max(m);
-  float l = 0.f, acc = 0.f;
+  const int g = lane >> 4, j = lane & 15;
+  float l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < splits; s0 += 64) {
     const int sl = s0 + lane;
     const float wl = sl < splits ? __builtin_amdgcn_exp2f(ml[2 * sl] - m) : 0.f;
     l += wave_sum(sl < splits ? wl * ml[2 * sl + 1] : 0.f);
     const int cnt = splits - s0 < 64 ? splits - s0 : 64;
-    const float* pos = po + (int64_t)s0 * 64 + lane;
-    int s = 0;
-    for (; s + 4 <= cnt; s += 4) {
-      const float o0 = pos[(s + 0) * 64], o1 = pos[(s + 1) * 64];
-      const float o2 = pos[(s + 2) * 64], o3 = pos[(s + 3) * 64];
-      acc = __builtin_fmaf(__shfl(wl, s + 0, 64), o0, acc);
-      acc = __builtin_fmaf(__shfl(wl, s + 1, 64), o1, acc);
-      acc = __builtin_fmaf(__shfl(wl, s + 2, 64), o2, acc);
-      acc = __builtin_fmaf(__shfl(wl, s + 3, 64), o3, acc);
+    const f32x4* pos = reinterpret_cast<const f32x4*>(po + (int64_t)s0 * 64) + j;
+    f32x4 o[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int s = g + 4 * i;
+      o[i] = s < cnt ? pos[s * 16] : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    for (; s < cnt; ++s) acc = __builtin_fmaf(__shfl(wl, s, 64), pos[s * 64], acc);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int s = g + 4 * i;
+      const float ws = __shfl(wl, s, 64);
+      if (s < cnt) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(ws, o[i][e], acc[e]);
+      }
+    }
   }
-  const float sv = fp8 ? s_v[bh] : 1.0f;
-  const _Float16 y = (_Float16)(acc * (sv / l));
-  out[((int64_t)b * rows + r) * H * 64 + h * 64 + lane] = __builtin_bit_cast(uint16_t, y);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    acc[e] += __shfl_xor(acc[e], 16, 64);
+    acc[e] += __shfl_xor(acc[e], 32, 64);
+  }
+  if (g == 0) {
+    const float f = (fp8 ? s_v[bh] : 1.0f) / l;
+    f16x4 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = (_Float16)(acc[e] * f);
+    *reinterpret_cast<f16x4*>(out + ((int64_t)b * rows + r) * H * 64 + h * 64 + 4 * j) = y;
+  }
 }
 
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, int prec, bool split, hipStream_t s) {
-  // FP8: wide query tiles (2 x 32 rows per wave) when there are many rows.
-  // FP16 keeps one 32-row group per wave (its Q fragment is twice as large).
-  const bool wide = prec == kPrecFp8 && a.q_rows_valid > 128;
-  const int qt = kWaves * 32 * (wide ? 2 : 1);
+  // FP8 takes two 32-row query groups per wavefront (more MFMA work per LDS
+  // read and per softmax step); split-KV calls with at most 128 rows use
+  // two-wavefront workgroups so that one small query batch still fills the
+  // chip.  FP16 keeps one group per wavefront (its Q fragment is twice as
+  // large).
   const int64_t rows = split ? a.q_rows_valid : a.out_rows;
-  const dim3 grid((unsigned)((rows + qt - 1) / qt), (unsigned)a.splits, (unsigned)a.bh_count);
-#define SDM_ATT(P, G, S) hipLaunchKernelGGL((attention_kernel<P, G, S>), grid, dim3(kThreads), 0, s, a)
+  auto go = [&](auto kern, int qt, int waves) {
+    const dim3 grid((unsigned)((rows + qt - 1) / qt), (unsigned)a.splits, (unsigned)a.bh_count);
+    hipLaunchKernelGGL(kern, grid, dim3(waves * 64), 0, s, a);
+  };
   if (prec == kPrecFp8) {
-    if (wide) { if (split) SDM_ATT(kPrecFp8, 2, true); else SDM_ATT(kPrecFp8, 2, false); }
-    else { if (split) SDM_ATT(kPrecFp8, 1, true); else SDM_ATT(kPrecFp8, 1, false); }
+    if (split) {
+      if (a.q_rows_valid <= 128) go(attention_kernel<kPrecFp8, 2, true, 2>, 128, 2);
+      else go(attention_kernel<kPrecFp8, 2, true, 4>, 256, 4);
+    } else {
+      if (a.q_rows_valid <= 128) go(attention_kernel<kPrecFp8, 1, false, 4>, 128, 4);
+      else go(attention_kernel<kPrecFp8, 2, false, 4>, 256, 4);
+    }
   } else {
-    if (split) SDM_ATT(kPrecFp16, 1, true); else SDM_ATT(kPrecFp16, 1, false);
+    if (split) go(attention_kernel<kPrecFp16, 1, true, 4>, 128, 4);
+    else go(attention_kernel<kPrecFp16, 1, false, 4>, 128, 4);
   }
-#undef SDM_ATT
   return hipGetLastError();
 }
 

@@ -44,7 +44,10 @@ constexpr uint64_t kMagic = 0x5344'4D49'434C'4131ull;  // "SDMICLA1"
 constexpr int64_t kFp8MinRows = 8192;
 // KV splits per cache: 3/8 of the CU count (96 on 256 CUs), i.e. three
 // 4-wave workgroups per CU for every head of a 128-row query batch.
-constexpr int kSplitsPer8Cus = 3;
+// Split-KV plan: about kBlocksPerCu two-wavefront workgroups per CU over all
+// (b, h) of a small query batch, i.e. two wavefronts per SIMD, the occupancy
+// the register budget of the query kernel allows.
+constexpr int kBlocksPerCu = 4;
 constexpr int64_t kMinTilesPerSplit = 4;
 
 thread_local std::string g_error;
@@ -105,9 +108,11 @@ int32_t resolve_precision(int64_t n, int32_t requested) {
   return requested;
 }
 
-void plan_splits(int64_t n, int32_t num_cus, int32_t* splits, int64_t* tiles_per_split) {
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+void plan_splits(int64_t n, int32_t num_cus, int64_t bh, int32_t* splits, int64_t* tiles_per_split) {
   const int64_t tiles = (n + kKeyTile - 1) / kKeyTile;
-  int64_t target = (int64_t)num_cus * kSplitsPer8Cus / 8;
+  int64_t target = ((int64_t)num_cus * kBlocksPerCu + bh - 1) / bh;
   if (target < 1) target = 1;
   int64_t tps = (tiles + target - 1) / target;
   if (tps < kMinTilesPerSplit) tps = kMinTilesPerSplit;
@@ -258,12 +263,13 @@ sdm_icl_status sdm_icl_head_factors(int64_t n, const float* head_coef, int32_t h
 
 int32_t sdm_icl_select_precision(int64_t n, int32_t requested) { return resolve_precision(n, requested); }
 
-sdm_icl_status sdm_icl_split_plan(int64_t n, int32_t num_cus, int32_t* kv_splits,
+sdm_icl_status sdm_icl_split_plan(int64_t n, int32_t num_cus, int32_t bh_count, int32_t* kv_splits,
                                   int64_t* keys_per_split) {
   if (!kv_splits || !keys_per_split) return fail(SDM_ICL_E_INVALID, "split_plan: null pointer");
-  if (n < 1 || num_cus < 1) return fail(SDM_ICL_E_INVALID, "split_plan: need n >= 1 and num_cus >= 1");
+  if (n < 1 || num_cus < 1 || bh_count < 1)
+    return fail(SDM_ICL_E_INVALID, "split_plan: need n, num_cus and bh_count >= 1");
   int64_t tps;
-  plan_splits(n, num_cus, kv_splits, &tps);
+  plan_splits(n, num_cus, bh_count, kv_splits, &tps);
   *keys_per_split = tps * kKeyTile;
   return SDM_ICL_OK;
 }
@@ -292,6 +298,13 @@ sdm_icl_status sdm_icl_attn_fit(const sdm_icl_fit_args* a, sdm_icl_cache* out) {
     return fail(SDM_ICL_E_INVALID, "fit: unknown precision %d", a->precision);
   if ((int64_t)a->batch * a->rows_padded * a->heads > (int64_t)1 << 40)
     return fail(SDM_ICL_E_INVALID, "fit: problem too large");
+  {
+    const void* p16[] = {a->q, a->k, a->v, a->out_ctx};
+    const char* n16[] = {"q", "k", "v", "out_ctx"};
+    for (int i = 0; i < 4; ++i)
+      if (!aligned(p16[i], 16)) return fail(SDM_ICL_E_INVALID, "fit: %s must be 16-byte aligned", n16[i]);
+    if (!aligned(a->gate, 2)) return fail(SDM_ICL_E_INVALID, "fit: gate must be 2-byte aligned");
+  }
 
   // ---- device checks
   int dev;
@@ -319,7 +332,7 @@ sdm_icl_status sdm_icl_attn_fit(const sdm_icl_fit_args* a, sdm_icl_cache* out) {
   c->L32 = length_scalar(n);
   if (a->scale_mode != SDM_ICL_SCALE_NONE) head_factors(n, a->head_coef, H, &c->kh);
   else std::memset(&c->kh, 0, sizeof c->kh);
-  plan_splits(n, di.cus, &c->splits, &c->tiles_per_split);
+  plan_splits(n, di.cus, (int64_t)B * H, &c->splits, &c->tiles_per_split);
 
   const size_t kv_bytes = (size_t)B * H * c->n_alloc * kHeadDim * eb;
   const size_t sc_bytes = (size_t)6 * B * H * sizeof(float);
@@ -417,6 +430,9 @@ sdm_icl_status sdm_icl_attn_query(sdm_icl_cache c, const void* q, const void* ga
                                        : "query: the cache was not fitted with GATED_LOG; gate must be NULL");
   if (R == 0) return SDM_ICL_OK;
   if (!q || !out || !ws) return fail(SDM_ICL_E_INVALID, "query: q, out and workspace are required");
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(ws, 16))
+    return fail(SDM_ICL_E_INVALID, "query: q, out and workspace must be 16-byte aligned");
+  if (!aligned(gate, 2)) return fail(SDM_ICL_E_INVALID, "query: gate must be 2-byte aligned");
   if ((int64_t)c->B * R * c->H > (int64_t)1 << 40) return fail(SDM_ICL_E_INVALID, "query: too many rows");
   const QueryLayout L = query_layout(c, R);
   if (ws_bytes < L.total)
@@ -591,6 +607,10 @@ sdm_icl_status sdm_icl_log_scale(const void* q, const void* gate, int32_t batch,
     return fail(SDM_ICL_E_INVALID, "log_scale: head_coef must be given exactly when scale_mode is LOG or GATED_LOG");
   if (rows == 0) return SDM_ICL_OK;
   if (!q || !out) return fail(SDM_ICL_E_INVALID, "log_scale: q and out are required");
+  if (!aligned(q, 16) || !aligned(out, 16))
+    return fail(SDM_ICL_E_INVALID, "log_scale: q and out must be 16-byte aligned");
+  if (!aligned(gate, 2)) return fail(SDM_ICL_E_INVALID, "log_scale: gate must be 2-byte aligned");
+  if (!aligned(q_inv_scale, 4)) return fail(SDM_ICL_E_INVALID, "log_scale: q_inv_scale must be 4-byte aligned");
   int dev;
   DeviceInfo di;
   sdm_icl_status st = current_device(&dev, &di);

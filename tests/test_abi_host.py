@@ -65,14 +65,20 @@ def test_precision_rule_matches_oracle():
             assert B.sdm_icl_select_precision(n, req) == icl.select_precision(n, req)
 
 
-def test_split_plan_is_a_function_of_n_only():
+def test_split_plan_depends_on_n_cus_and_heads_only():
     for n in (1, 63, 64, 65, 1000, 16384, 131072, 523288, 524288):
-        s, kps = B.sdm_icl_split_plan(n, 256)
-        assert kps % 64 == 0 and s >= 1
-        assert (s - 1) * kps < n <= s * kps   # every split holds at least one valid key
-    assert B.sdm_icl_split_plan(524288, 256) == (96, 5504)
-    with pytest.raises(B.SdmIclError):
-        B.sdm_icl_split_plan(0, 256)
+        for bh in (1, 4, 8, 16, 200):
+            s, kps = B.sdm_icl_split_plan(n, 256, bh)
+            assert kps % 64 == 0 and s >= 1
+            assert (s - 1) * kps < n <= s * kps   # every split holds at least one valid key
+            assert kps >= min(256, -(-n // 64) * 64)  # at least 4 tiles unless n is shorter
+    # 8 heads on 256 CUs: 128 splits x 8 heads = 4 two-wavefront workgroups per CU
+    assert B.sdm_icl_split_plan(524288, 256, 8) == (128, 4096)
+    assert B.sdm_icl_split_plan(523288, 256, 8) == (128, 4096)
+    assert B.sdm_icl_split_plan(524288, 256, 4) == (256, 2048)
+    for bad in ((0, 256, 8), (100, 0, 8), (100, 256, 0)):
+        with pytest.raises(B.SdmIclError):
+            B.sdm_icl_split_plan(*bad)
 
 
 def _fit_args(**kw):
@@ -101,6 +107,10 @@ def _fit_args(**kw):
     (dict(scale_mode=0, head_coef="set"), 1),          # coefficients without scaling
     (dict(precision=5), 1),
     (dict(rows_padded=50), 1),                         # n = 100 > N_pad
+    (dict(q=0x1008), 1),                               # q not 16-byte aligned
+    (dict(v=0x3002), 1),
+    (dict(out_ctx=0x5004), 1),
+    (dict(scale_mode=2, head_coef="set", gate=0x4001), 1),  # odd gate address
 ])
 def test_fit_rejects_bad_arguments_before_any_device_work(kw, status):
     args, keep = _fit_args(**kw)
