@@ -63,6 +63,14 @@ class Workload:
     nan_tail: bool = False
     query_batches: tuple = ()
     description: str = ""
+    lengths: tuple = ()          # per-batch valid rows (empty: every element has n_valid)
+
+    def valid_rows(self, b: int) -> int:
+        """Valid context rows of batch element b."""
+        return int(self.lengths[b]) if self.lengths else self.n_valid
+
+    def length_list(self) -> list:
+        return [self.valid_rows(b) for b in range(self.batch)]
 
 
 # The five workloads: tiny FP16, 16K LogScale/GatedLogScale FP16, 128K FP8,
@@ -170,10 +178,12 @@ def make_inputs(w: Workload) -> Inputs:
     if w.outliers:
         for t in (q_ctx, k_ctx, v_ctx, q_query):
             _add_outliers(rng, t)
-    if w.nan_tail and w.n_valid < N:
-        for t in (q_ctx, k_ctx, v_ctx):
-            t[:, w.n_valid:] = np.float16(np.nan)
-        gate_ctx[:, w.n_valid:] = np.float16(np.nan)
+    if w.nan_tail:
+        for b in range(B):
+            nb = w.valid_rows(b)
+            for t in (q_ctx, k_ctx, v_ctx):
+                t[b, nb:] = np.float16(np.nan)
+            gate_ctx[b, nb:] = np.float16(np.nan)
     return Inputs(w, q_ctx, k_ctx, v_ctx, q_query, head_coef, gate_ctx, gate_query)
 
 

@@ -29,6 +29,10 @@ reason in the design notes of the repository):
   context queries; query rows reuse it (and saturate above it).
 * masked context rows (index >= n) are not keys, not part of n and not part
   of any amax; their outputs are zero.
+* per-batch lengths (the pages' fused path covers one shared int and falls
+  back for tensor lengths): element b behaves as a batch of one with n_b
+  rows (its own length scalar, head factors, FP8 scales and keys); AUTO
+  precision follows the longest context of the call.
 """
 from __future__ import annotations
 
@@ -183,35 +187,67 @@ def attention_rows(qhat: np.ndarray, khat: np.ndarray, vhat: np.ndarray,
 
 @dataclass
 class OracleCache:
-    """What ``fit`` keeps: the key length, scaling factors and the K/V operands."""
+    """What ``fit`` keeps per batch element b: its key length n_b, scaling
+    factors and K/V operands (valid rows only)."""
 
-    n: int
+    lengths: np.ndarray              # int64 [B]: n_b
     heads: int
     head_dim: int
     scale_mode: int
     precision: int
-    L32: np.float32
-    k_h: Optional[np.ndarray]        # fp16 [H] or None
+    L32s: np.ndarray                 # float32 [B]
+    k_hs: Optional[np.ndarray]       # fp16 [B, H] or None
     scales: np.ndarray               # float32 [3, B, H]: s_q, s_k, s_v (ones for FP16)
     inv: np.ndarray                  # float32 [3, B, H]
-    k16: np.ndarray                  # fp16 [B, n, H, D] (valid rows only)
-    v16: np.ndarray
-    k_codes: Optional[np.ndarray]    # uint8 [B, H, n, D] (FP8 only)
-    v_codes: Optional[np.ndarray]
+    k16: list                        # per b: fp16 [n_b, H, D]
+    v16: list
+    k_codes_b: Optional[list]        # per b: uint8 [H, n_b, D] (FP8 only)
+    v_codes_b: Optional[list]
 
     @property
     def tau(self) -> float:
         return 1.0 / math.sqrt(self.head_dim)
 
+    def _shared(self) -> None:
+        if np.any(self.lengths != self.lengths[0]):
+            raise ValueError("the batch elements have different lengths")
+
+    @property
+    def n(self) -> int:
+        """The shared length (only when every batch element has the same n)."""
+        self._shared()
+        return int(self.lengths[0])
+
+    @property
+    def L32(self) -> np.float32:
+        self._shared()
+        return self.L32s[0]
+
+    @property
+    def k_h(self) -> Optional[np.ndarray]:
+        self._shared()
+        return None if self.k_hs is None else self.k_hs[0]
+
+    @property
+    def k_codes(self) -> Optional[np.ndarray]:
+        """uint8 ``[B, H, n, D]`` (shared length only)."""
+        self._shared()
+        return None if self.k_codes_b is None else np.stack(self.k_codes_b)
+
+    @property
+    def v_codes(self) -> Optional[np.ndarray]:
+        self._shared()
+        return None if self.v_codes_b is None else np.stack(self.v_codes_b)
+
     def khat(self, b: int, h: int) -> np.ndarray:
         if self.precision == PREC_FP8_E4M3:
-            return E4M3_VALUES[self.k_codes[b, h]] * np.float64(self.scales[1, b, h])
-        return self.k16[b, :, h, :].astype(np.float64)
+            return E4M3_VALUES[self.k_codes_b[b][h]] * np.float64(self.scales[1, b, h])
+        return self.k16[b][:, h, :].astype(np.float64)
 
     def vhat(self, b: int, h: int) -> np.ndarray:
         if self.precision == PREC_FP8_E4M3:
-            return E4M3_VALUES[self.v_codes[b, h]] * np.float64(self.scales[2, b, h])
-        return self.v16[b, :, h, :].astype(np.float64)
+            return E4M3_VALUES[self.v_codes_b[b][h]] * np.float64(self.scales[2, b, h])
+        return self.v16[b][:, h, :].astype(np.float64)
 
     def qhat(self, qt: np.ndarray, b: int, h: int) -> np.ndarray:
         """Operand used for scaled query rows qt ``[m, H, D]`` (fp16) of head h."""
@@ -221,35 +257,60 @@ class OracleCache:
         return x.astype(np.float64)
 
 
-def fit(q: np.ndarray, k: np.ndarray, v: np.ndarray, n: int, scale_mode: int,
+def _lengths(n, B: int, N: int) -> np.ndarray:
+    """n as one int64 per batch element: a shared int, or a sequence of B."""
+    arr = np.asarray(n, dtype=np.int64).reshape(-1)
+    if arr.size == 1:
+        arr = np.full(B, arr[0], dtype=np.int64)
+    if arr.size != B:
+        raise ValueError("lengths must be one int or one per batch element")
+    if np.any(arr < 1) or np.any(arr > N):
+        raise ValueError("need 1 <= n_b <= N_pad")
+    return arr
+
+
+def fit(q: np.ndarray, k: np.ndarray, v: np.ndarray, n, scale_mode: int,
         precision: int, head_coef: Optional[np.ndarray] = None,
         gate: Optional[np.ndarray] = None, keep_codes: bool = True) -> OracleCache:
-    """Build the cache from context Q/K/V ``[B, N_pad, H, D]`` with n valid rows."""
+    """Build the cache from context Q/K/V ``[B, N_pad, H, D]``.
+
+    n: the valid rows, one int shared by all batch elements or one per
+    element.  Element b is treated exactly as a batch of one with n_b valid
+    rows: its own length scalar and head factors, FP8 scales over its own
+    valid rows, its own keys.  AUTO precision is decided once for the call by
+    the longest context (FP8 iff max n_b > 8,192).
+    """
     B, N, H, D = q.shape
-    if not 1 <= n <= N:
-        raise ValueError("need 1 <= n <= N_pad")
-    prec = select_precision(n, precision)
-    L32 = length_scalar(n)
-    k_h = head_factors(L32, head_coef) if scale_mode != SCALE_NONE else None
+    lengths = _lengths(n, B, N)
+    prec = select_precision(int(lengths.max()), precision)
+    L32s = np.array([length_scalar(int(nb)) for nb in lengths], dtype=np.float32)
+    k_hs = (np.stack([head_factors(L32s[b], head_coef) for b in range(B)])
+            if scale_mode != SCALE_NONE else None)
     scales = np.ones((3, B, H), dtype=np.float32)
     inv = np.ones((3, B, H), dtype=np.float32)
     k_codes = v_codes = None
     if prec == PREC_FP8_E4M3:
-        k_codes = np.empty((B, H, n, D), dtype=np.uint8)
-        v_codes = np.empty((B, H, n, D), dtype=np.uint8)
+        k_codes, v_codes = [], []
         for b in range(B):
-            qt = scale_queries(q[b, :n], scale_mode, k_h,
-                               None if gate is None else gate[b, :n])
-            for t, x in enumerate((qt, k[b, :n], v[b, :n])):
+            nb = int(lengths[b])
+            qt = scale_queries(q[b, :nb], scale_mode, None if k_hs is None else k_hs[b],
+                               None if gate is None else gate[b, :nb])
+            for t, x in enumerate((qt, k[b, :nb], v[b, :nb])):
                 a = amax_rows(x)
                 for h in range(H):
                     scales[t, b, h], inv[t, b, h] = fp8_scale(a[h])
+            kc = np.empty((H, nb, D), dtype=np.uint8)
+            vc = np.empty((H, nb, D), dtype=np.uint8)
             for h in range(H):
-                k_codes[b, h] = quantize_codes(k[b, :n, h, :], inv[1, b, h])
-                v_codes[b, h] = quantize_codes(v[b, :n, h, :], inv[2, b, h])
-    return OracleCache(n=n, heads=H, head_dim=D, scale_mode=scale_mode, precision=prec,
-                       L32=L32, k_h=k_h, scales=scales, inv=inv,
-                       k16=k[:, :n], v16=v[:, :n], k_codes=k_codes, v_codes=v_codes)
+                kc[h] = quantize_codes(k[b, :nb, h, :], inv[1, b, h])
+                vc[h] = quantize_codes(v[b, :nb, h, :], inv[2, b, h])
+            k_codes.append(kc)
+            v_codes.append(vc)
+    return OracleCache(lengths=lengths, heads=H, head_dim=D, scale_mode=scale_mode, precision=prec,
+                       L32s=L32s, k_hs=k_hs, scales=scales, inv=inv,
+                       k16=[k[b, :int(lengths[b])] for b in range(B)],
+                       v16=[v[b, :int(lengths[b])] for b in range(B)],
+                       k_codes_b=k_codes, v_codes_b=v_codes)
 
 
 def attend(cache: OracleCache, q_rows: np.ndarray, gate_rows: Optional[np.ndarray],
@@ -257,11 +318,13 @@ def attend(cache: OracleCache, q_rows: np.ndarray, gate_rows: Optional[np.ndarra
            block: int = 128) -> np.ndarray:
     """Outputs (float64 ``[m, H, D]``) of query rows ``q_rows [m, H, D]`` of batch b.
 
-    Rows are scaled with the cache's length and coefficients, quantised with
-    the cache's context-derived Q scale in FP8 mode, and attend to all n keys.
-    Rows are evaluated independently, ``block`` at a time to bound memory.
+    Rows are scaled with batch element b's length and the coefficients,
+    quantised with b's context-derived Q scale in FP8 mode, and attend to b's
+    n_b keys.  Rows are evaluated independently, ``block`` at a time to bound
+    memory.
     """
-    qt = scale_queries(q_rows, cache.scale_mode, cache.k_h, gate_rows)
+    qt = scale_queries(q_rows, cache.scale_mode, None if cache.k_hs is None else cache.k_hs[b],
+                       gate_rows)
     m = q_rows.shape[0]
     out = np.zeros((m, cache.heads, cache.head_dim), dtype=np.float64)
     for h in (range(cache.heads) if heads is None else heads):
@@ -274,10 +337,10 @@ def attend(cache: OracleCache, q_rows: np.ndarray, gate_rows: Optional[np.ndarra
 
 def context_outputs(cache: OracleCache, q: np.ndarray, gate: Optional[np.ndarray],
                     rows: Sequence[int], b: int = 0, heads=None) -> np.ndarray:
-    """Self-attention outputs of the given context rows (masked rows give 0)."""
+    """Self-attention outputs of batch b's given context rows (rows >= n_b give 0)."""
     rows = np.asarray(rows, dtype=np.int64)
     out = np.zeros((rows.size, cache.heads, cache.head_dim), dtype=np.float64)
-    valid = rows < cache.n
+    valid = rows < cache.lengths[b]
     if np.any(valid):
         g = None if gate is None else gate[b, rows[valid]]
         out[valid] = attend(cache, q[b, rows[valid]], g, b=b, heads=heads)

@@ -232,6 +232,72 @@ def test_masked_rows_are_ignored():
     assert np.all(o[3:] == 0)
 
 
+def _ragged(batch_lengths, n_pad, **kw):
+    from dataclasses import replace
+    w = replace(gen.WORKLOADS["cached512k_fp8_gated"], name="ragged", seed=11, n_pad=n_pad,
+                n_valid=max(batch_lengths), n_query=24, batch=len(batch_lengths),
+                lengths=tuple(batch_lengths), nan_tail=True, **kw)
+    return gen.make_inputs(w)
+
+
+@pytest.mark.parametrize("mode,prec", [(icl.SCALE_GATED_LOG, icl.PREC_FP8_E4M3),
+                                       (icl.SCALE_LOG, icl.PREC_FP16)])
+def test_per_batch_lengths_equal_separate_fits(mode, prec):
+    """A batch with lengths (n_0, n_1, n_2) gives, element by element, exactly
+    what a batch of one with that element and its own n_b gives: length
+    scalar, head factors, FP8 scales and codes, context and query outputs.
+    Using one shared length, or taking an amax across the batch, fails it."""
+    lengths = [900, 333, 64]
+    x = _ragged(lengths, 1024)
+    gate = x.gate_ctx if mode == icl.SCALE_GATED_LOG else None
+    gq = x.gate_query if mode == icl.SCALE_GATED_LOG else None
+    c = icl.fit(x.q_ctx, x.k_ctx, x.v_ctx, lengths, mode, prec, x.head_coef, gate)
+    assert list(c.lengths) == lengths
+    with pytest.raises(ValueError):
+        c.n
+    for b, nb in enumerate(lengths):
+        sl = slice(b, b + 1)
+        one = icl.fit(x.q_ctx[sl], x.k_ctx[sl], x.v_ctx[sl], nb, mode, prec, x.head_coef,
+                      None if gate is None else gate[sl])
+        assert c.L32s[b] == one.L32 == icl.length_scalar(nb)
+        np.testing.assert_array_equal(c.k_hs[b], one.k_h)
+        np.testing.assert_array_equal(c.scales[:, b], one.scales[:, 0])
+        if prec == icl.PREC_FP8_E4M3:
+            np.testing.assert_array_equal(c.k_codes_b[b], one.k_codes[0])
+            np.testing.assert_array_equal(c.v_codes_b[b], one.v_codes[0])
+        rows = [0, nb // 2, nb - 1, nb, 1023]
+        np.testing.assert_array_equal(
+            icl.context_outputs(c, x.q_ctx, gate, rows, b=b, heads=[0, 5]),
+            icl.context_outputs(one, x.q_ctx[sl], None if gate is None else gate[sl], rows, heads=[0, 5]))
+        np.testing.assert_array_equal(
+            icl.attend(c, x.q_query[b], None if gq is None else gq[b], b=b, heads=[2]),
+            icl.attend(one, x.q_query[b], None if gq is None else gq[b], heads=[2]))
+    # the element lengths differ, so their length scalars differ
+    assert len(set(c.L32s.tolist())) == 3
+
+
+def test_per_batch_masked_rows_are_zero_and_ignored():
+    lengths = [700, 129]
+    x = _ragged(lengths, 768)
+    assert np.isnan(x.k_ctx[1, 129]).all() and np.isfinite(x.k_ctx[1, 128]).all()
+    c = icl.fit(x.q_ctx, x.k_ctx, x.v_ctx, lengths, icl.SCALE_GATED_LOG, icl.PREC_FP8_E4M3,
+                x.head_coef, x.gate_ctx)
+    assert np.all(np.isfinite(c.scales))
+    o = icl.context_outputs(c, x.q_ctx, x.gate_ctx, [0, 128, 129, 700, 767], b=1, heads=[1])
+    assert np.all(np.isfinite(o[:2])) and np.all(o[2:] == 0)
+
+
+def test_auto_precision_follows_the_longest_context():
+    for lengths, want in (([100, 8193], icl.PREC_FP8_E4M3), ([8192, 100], icl.PREC_FP16)):
+        B, N, H, D = 2, 8200, 1, 64
+        z = np.zeros((B, N, H, D), dtype=np.float16)
+        assert icl.fit(z, z, z, lengths, icl.SCALE_NONE, icl.PREC_AUTO).precision == want
+    with pytest.raises(ValueError):
+        icl.fit(z, z, z, [0, 5], icl.SCALE_NONE, icl.PREC_FP16)
+    with pytest.raises(ValueError):
+        icl.fit(z, z, z, [5, 5, 5], icl.SCALE_NONE, icl.PREC_FP16)
+
+
 def test_fp8_is_lossless_on_grid_inputs():
     """I10: when Q~, K, V already lie on the e4m3 grid with amax = 448 s, FP8
     quantisation changes nothing and the FP8 result equals the FP16 one.  Each
