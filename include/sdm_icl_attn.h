@@ -61,7 +61,7 @@ extern "C" {
 typedef int32_t sdm_icl_status;
 #define SDM_ICL_OK            0
 #define SDM_ICL_E_INVALID     1  /* bad argument: null pointer, size, mode/gate mismatch */
-#define SDM_ICL_E_UNSUPPORTED 2  /* valid but not implemented (head_dim != 64, per-batch lengths) */
+#define SDM_ICL_E_UNSUPPORTED 2  /* valid but not implemented (head_dim != 64, > 128 heads) */
 #define SDM_ICL_E_DEVICE      3  /* pointer not on the stream's device, or not a gfx950 device */
 #define SDM_ICL_E_OOM         4  /* device allocation failed */
 #define SDM_ICL_E_HIP         5  /* a HIP runtime call failed */
@@ -84,10 +84,14 @@ typedef struct {
   int32_t rows_padded;     /* N_pad >= 1: allocated context rows per batch element */
   int32_t heads;           /* H, 1..128 */
   int32_t head_dim;        /* D, must be 64 */
-  const int64_t* lengths;  /* host [B]: valid rows n_b, 1 <= n_b <= N_pad; all equal (one
-                              shared length, as the fused scaling path requires); rows
-                              n..N_pad-1 are masked: not keys, not in n, not in any amax,
-                              their outputs are 0 and their contents are never read */
+  const int64_t* lengths;  /* host [B]: valid rows n_b, 1 <= n_b <= N_pad, one per batch
+                              element (equal values = one shared length, the case the
+                              pages' fused scaling covers; differing values make each
+                              element behave as a batch of one with its own n_b, L32(n_b)
+                              and k_h).  Rows n_b..N_pad-1 of element b are masked: not
+                              keys, not in n_b, not in any amax, their outputs are 0 and
+                              their contents are never read.  AUTO precision follows the
+                              longest context, max n_b. */
   const void* q;           /* device fp16 [B, N_pad, H, D], row-major, row stride H*D */
   const void* k;           /* device fp16 [B, N_pad, H, D] */
   const void* v;           /* device fp16 [B, N_pad, H, D] */
@@ -105,10 +109,10 @@ typedef struct {
   int32_t precision;       /* resolved: FP16 or FP8_E4M3, never AUTO */
   int32_t scale_mode;
   int32_t kv_splits;       /* KV-axis split count used by every query call (fixed at fit) */
-  int64_t n_valid;         /* n */
-  int64_t rows_alloc;      /* cache rows per (b, h): n rounded up to the 64-row key tile */
+  int64_t n_valid;         /* n (per-batch lengths: the longest, max n_b) */
+  int64_t rows_alloc;      /* cache rows per (b, h): n_valid rounded up to the 64-row key tile */
   int64_t keys_per_split;  /* rows of each KV split (multiple of 64) */
-  float length_scalar;     /* L32 */
+  float length_scalar;     /* L32 (per-batch lengths: that of batch element 0) */
   uint64_t device_bytes;   /* bytes of device memory the cache holds */
 } sdm_icl_cache_info;
 
@@ -124,7 +128,8 @@ sdm_icl_status sdm_icl_attn_fit(const sdm_icl_fit_args* args, sdm_icl_cache* out
 sdm_icl_status sdm_icl_attn_query_workspace_size(sdm_icl_cache cache, int64_t n_query,
                                                  size_t* bytes);
 
-/* Query rows attend to the cached context (model.predict).  q: device fp16
+/* Query rows attend to the cached context (model.predict); the rows of batch
+ * element b attend to its n_b cached keys, scaled with its L32(n_b).  q: device fp16
  * [B, R, H, D]; gate: device fp16 [B, R, H], non-NULL iff the cache was fitted
  * with GATED_LOG (otherwise SDM_ICL_E_INVALID, the analogue of misusing an FP8
  * cache outside its scope); out: device fp16 [B, R, H, D].  workspace: caller
@@ -140,8 +145,14 @@ sdm_icl_status sdm_icl_attn_query(sdm_icl_cache cache, const void* q, const void
 /* Shape, precision and split plan of a cache. */
 sdm_icl_status sdm_icl_attn_cache_info(sdm_icl_cache cache, sdm_icl_cache_info* info);
 
+/* Per-batch lengths n_b (host int64 [B]) and their length scalars L32(n_b)
+ * (host float32 [B]) of a cache; either pointer may be NULL. */
+sdm_icl_status sdm_icl_attn_cache_lengths(sdm_icl_cache cache, int64_t* host_lengths,
+                                          float* host_length_scalars);
+
 /* Copy the cached operands to host memory (parity checks, persistence).
- * host_k / host_v: [B, H, n, D] elements, 1 byte (e4m3 code) in FP8 mode or
+ * host_k / host_v: [B, H, n, D] elements with n = n_valid (rows n_b..n-1 of a
+ * shorter batch element are 0), 1 byte (e4m3 code) in FP8 mode or
  * 2 bytes (fp16) in FP16 mode; host_scales: float32 [3, B, H] = s_q, s_k, s_v
  * (all 1 in FP16 mode).  Any of the three may be NULL.  Synchronises `stream`. */
 sdm_icl_status sdm_icl_attn_cache_export(sdm_icl_cache cache, void* host_k, void* host_v,
@@ -202,7 +213,9 @@ int32_t sdm_icl_select_precision(int64_t n, int32_t requested);
 /* KV split plan for n valid keys and bh_count = batch * heads on a device with
  * num_cus compute units: about 4 * num_cus / bh_count splits of at least 4
  * key tiles each.  A pure function of (n, num_cus, bh_count), never of the
- * query count, so every query batch of a cache uses the same plan. */
+ * query count, so every query batch of a cache uses the same plan.  A cache
+ * with per-batch lengths plans for the longest, max n_b; the splits past a
+ * shorter element's n_b hold no keys of it and weigh 0 in its combine. */
 sdm_icl_status sdm_icl_split_plan(int64_t n, int32_t num_cus, int32_t bh_count, int32_t* kv_splits,
                                   int64_t* keys_per_split);
 

@@ -61,6 +61,8 @@ _SIGNATURES = {
     "sdm_icl_attn_cache_info": (ctypes.c_int32, [ctypes.c_void_p, ctypes.POINTER(CacheInfo)]),
     "sdm_icl_attn_cache_export": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                                    ctypes.c_void_p, ctypes.c_void_p]),
+    "sdm_icl_attn_cache_lengths": (ctypes.c_int32, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
+                                                    ctypes.POINTER(ctypes.c_float)]),
     "sdm_icl_attn_release": (ctypes.c_int32, [ctypes.c_void_p]),
     "sdm_icl_log_scale": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                            ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
@@ -195,12 +197,13 @@ class Cache:
         self.release()
 
 
-def sdm_icl_attn_fit(q, k, v, length: int, scale_mode: int = SDM_ICL_SCALE_NONE,
+def sdm_icl_attn_fit(q, k, v, length, scale_mode: int = SDM_ICL_SCALE_NONE,
                      precision: int = SDM_ICL_PREC_AUTO, head_coef=None, gate=None,
                      out_ctx=None, stream=None) -> Cache:
     """Build the K/V cache from context q/k/v ``[B, N_pad, H, 64]`` (fp16) with
-    ``length`` valid rows; if ``out_ctx`` (same shape) is given, the context
-    self-attention is written there too."""
+    ``length`` valid rows (one int for every batch element, or a sequence of
+    B ints); if ``out_ctx`` (same shape) is given, the context self-attention
+    is written there too."""
     import torch
     if q.dim() != 4:
         raise ValueError("q must be [B, N_pad, H, D]")
@@ -212,7 +215,12 @@ def sdm_icl_attn_fit(q, k, v, length: int, scale_mode: int = SDM_ICL_SCALE_NONE,
         raise ValueError("gate must be [B, N_pad, H]")
     if out_ctx is not None and tuple(out_ctx.shape) != (B, N, H, D):
         raise ValueError("out_ctx must have the shape of q")
-    lengths = (ctypes.c_int64 * B)(*([int(length)] * B))
+    ls = [int(x) for x in np.asarray(length, dtype=np.int64).reshape(-1)]
+    if len(ls) == 1:
+        ls = ls * B
+    if len(ls) != B:
+        raise ValueError("length must be one int or one per batch element")
+    lengths = (ctypes.c_int64 * B)(*ls)
     coef = None
     if head_coef is not None:
         coef_np = np.ascontiguousarray(head_coef, dtype=np.float32)
@@ -273,6 +281,16 @@ def sdm_icl_attn_cache_export(cache: Cache, stream=None):
     _check(lib().sdm_icl_attn_cache_export(cache.handle, k.ctypes.data, v.ctypes.data,
                                            sc.ctypes.data, _stream_ptr(stream)))
     return k, v, sc
+
+
+def sdm_icl_attn_cache_lengths(cache: Cache):
+    """(n_b int64 ``[B]``, L32(n_b) float32 ``[B]``) of a cache."""
+    B = sdm_icl_attn_cache_info(cache)["batch"]
+    n = np.empty(B, dtype=np.int64)
+    L = np.empty(B, dtype=np.float32)
+    _check(lib().sdm_icl_attn_cache_lengths(cache.handle, n.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                            L.ctypes.data_as(ctypes.POINTER(ctypes.c_float))))
+    return n, L
 
 
 def sdm_icl_attn_release(cache: Cache) -> None:

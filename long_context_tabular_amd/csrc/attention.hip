@@ -282,8 +282,10 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
   const int b = bh / a.heads, h = bh - b * a.heads;
   const int64_t q0 = (int64_t)blockIdx.x * QT;
   const int split = blockIdx.y;
+  const int64_t n = a.n_b[b];                          // keys of this batch element
+  const int64_t q_valid = a.ctx ? n : a.q_rows_valid;  // its valid query rows
 
-  if (q0 >= a.q_rows_valid) {
+  if (q0 >= q_valid) {
     if constexpr (!SPLIT) {
       // rows past the valid context: zeros (16 bytes per thread per step)
       const int64_t r_end = a.out_rows < q0 + QT ? a.out_rows : q0 + QT;
@@ -316,9 +318,24 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
     ws.o[g][1] = f32x16{};
   }
 
-  const int64_t n_tiles = a.n_alloc / 64;
+  const int64_t n_tiles = (n + 63) / 64;
   const int64_t t0 = (int64_t)split * a.tiles_per_split;
   const int64_t t1 = n_tiles < t0 + a.tiles_per_split ? n_tiles : t0 + a.tiles_per_split;
+  if (t0 >= n_tiles) {
+    // a batch element shorter than the split plan's longest one has no keys
+    // in this split: an empty partial (m = -inf, l = 0, O = 0) that the
+    // combine weighs with 0
+    if constexpr (SPLIT) {
+      const int64_t r_end = q_valid < q0 + QT ? q_valid : q0 + QT;
+      for (int64_t r = q0 + tid; r < r_end; r += NT) {
+        const int64_t slot = ((int64_t)bh * a.q_rows_valid + r) * a.splits + split;
+        *reinterpret_cast<float2*>(a.part_ml + slot * 2) = make_float2(-INFINITY, 0.f);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) reinterpret_cast<f32x4*>(a.part_o + slot * 64)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    return;
+  }
 
   const unsigned char* kg = reinterpret_cast<const unsigned char*>(a.kc) + (int64_t)bh * a.n_alloc * 64 * EB;
   const unsigned char* vg = reinterpret_cast<const unsigned char*>(a.vt) + (int64_t)bh * a.n_alloc * 64 * EB;
@@ -393,8 +410,8 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
   };
   // tiles [t0, t_full) hold only valid keys; a partial tile can only be the
   // context's last one
-  const int64_t t_full = (t1 * 64 > a.n) ? t1 - 1 : t1;
-  const int rem_last = (int)(a.n - (t1 - 1) * 64);
+  const int64_t t_full = (t1 * 64 > n) ? t1 - 1 : t1;
+  const int rem_last = (int)(n - (t1 - 1) * 64);
   if (t0 < t_full)
     attend_tile<PREC, QG, true, false>(ws, kbuf[0], vbuf[0], c_scale, col, hf, 64);
   else
@@ -426,7 +443,7 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
     const float l_tot = lo + hi;
     const int64_t q = wq0 + g * 32 + col;
     if constexpr (SPLIT) {
-      if (q < a.q_rows_valid) {
+      if (q < q_valid) {
         const int64_t slot = ((int64_t)bh * a.q_rows_valid + q) * a.splits + split;
         if (hf == 0) *reinterpret_cast<float2*>(a.part_ml + slot * 2) = make_float2(ws.m_run[g], l_tot);
 #pragma unroll
@@ -440,7 +457,7 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
       }
     } else {
       if (q < a.out_rows) {
-        const bool valid = q < a.q_rows_valid;
+        const bool valid = q < q_valid;
         const float f = valid ? sv / l_tot : 0.f;
         uint16_t* orow = a.out + (((int64_t)b * a.out_rows + q) * a.heads + h) * 64;
 #pragma unroll

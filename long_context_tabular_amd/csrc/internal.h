@@ -34,8 +34,10 @@ struct AttnArgs {
   int64_t q_rows_valid;   // query rows that exist (context: n; cached query: R)
   int64_t out_rows;       // final mode: rows per batch element of `out`; rows in
                           // [q_rows_valid, out_rows) are written as zeros
-  int64_t n;              // valid keys
-  int64_t n_alloc;        // cache rows per (b,h), multiple of kKeyTile
+  const int64_t* n_b;     // device [B]: valid keys of each batch element
+  int64_t n_alloc;        // cache rows per (b,h), multiple of kKeyTile (>= every n_b)
+  int32_t ctx;            // 1: the query rows are the context rows, so batch element b
+                          // has n_b valid query rows (q_rows_valid is then their maximum)
   int32_t tiles_per_split;
   int32_t splits;
   int32_t heads;
@@ -43,13 +45,21 @@ struct AttnArgs {
   float tau_log2e;        // log2(e) / sqrt(D)
 };
 
+// Per-(b,h) head factors k_h as fp16 bits: a device array [B*H] (kh_bh), or,
+// when kh_bh is NULL, the same factors for every batch element, by value.
+struct Factors {
+  const uint16_t* kh_bh;
+  HeadFactors kh;
+};
+
 // K0 + scale finalisation: per-(b,h) amax of the scaled context queries, K, V
-// over the first n rows, then s = amax/448, inv = 448/amax (1 if amax = 0)
-// into scales[0 .. 3BH) and inv[0 .. 3BH).  amax_bits: device scratch [3*B*H].
+// over the first n_b rows of batch element b (n_b: device [B], n_max their
+// maximum), then s = amax/448, inv = 448/amax (1 if amax = 0) into
+// scales[0 .. 3BH) and inv[0 .. 3BH).  amax_bits: device scratch [3*B*H].
 hipError_t launch_fp8_scales(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                             const uint16_t* gate, int B, int64_t rows_padded, int64_t n,
-                             int H, int mode, const HeadFactors& kh, uint32_t* amax_bits,
-                             float* scales, float* inv, hipStream_t s);
+                             const uint16_t* gate, int B, int64_t rows_padded, int64_t n_max,
+                             const int64_t* n_b, int H, int mode, const Factors& f,
+                             uint32_t* amax_bits, float* scales, float* inv, hipStream_t s);
 
 // Fill `count` floats with a value (FP16 caches get unit scales).
 hipError_t launch_fill_f32(float* p, int64_t count, float value, hipStream_t s);
@@ -57,15 +67,17 @@ hipError_t launch_fill_f32(float* p, int64_t count, float value, hipStream_t s);
 // K1: scale rows [0, rows_valid) of q [B][rows_in][H][64] (and gate [B][rows_in][H]),
 // optionally quantise with inv_q (device [B*H], NULL = keep fp16), and write
 // head-major out [B*H][rows_out][64]; rows in [rows_valid, rows_out) become 0.
+// rows_valid_b (device [B], may be NULL) gives batch element b its own
+// rows_valid.
 hipError_t launch_scale_queries(const uint16_t* q, const uint16_t* gate, int B, int64_t rows_in,
-                                int64_t rows_valid, int64_t rows_out, int H, int mode,
-                                const HeadFactors& kh, const float* inv_q, void* out,
+                                int64_t rows_valid, const int64_t* rows_valid_b, int64_t rows_out,
+                                int H, int mode, const Factors& f, const float* inv_q, void* out,
                                 hipStream_t s);
 
-// K2: K/V rows [0, n) -> cache (codes with inv_k / inv_v when prec == FP8, else
-// fp16 copies); rows in [n, n_alloc) become 0.
+// K2: K/V rows [0, n_b) of batch element b -> cache (codes with inv_k / inv_v
+// when prec == FP8, else fp16 copies); rows in [n_b, n_alloc) become 0.
 hipError_t launch_pack_kv(const uint16_t* k, const uint16_t* v, int B, int64_t rows_padded,
-                          int64_t n, int64_t n_alloc, int H, int prec, const float* inv_k,
+                          const int64_t* n_b, int64_t n_alloc, int H, int prec, const float* inv_k,
                           const float* inv_v, void* kc, void* vt, hipStream_t s);
 
 // K3 / K4: flash attention over the cache.  split == false writes normalised

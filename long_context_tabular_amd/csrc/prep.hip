@@ -5,8 +5,9 @@
 //
 // Scaling follows "Fuse shared-length query scaling during inference"
 // (Problem identified, Solution): one host-prepared float32 log-length per
-// launch, per-head factors converted to fp16, and every eager fp16 rounding
-// boundary kept, so results are bit-identical to the unfused sequence.
+// launch (one per batch element when the elements have their own lengths),
+// per-head factors converted to fp16, and every eager fp16 rounding boundary
+// kept, so results are bit-identical to the unfused sequence.
 // Quantisation follows "[FP8 3/4] Integrate FP8 attention and caching into
 // TabICLv2" (introduction): per-head scales from the context, with the Q scale
 // taken from the scaled context queries and reused for query rows.
@@ -83,6 +84,11 @@ __device__ inline float half_bits_to_float(uint16_t b) {
   return (float)__builtin_bit_cast(_Float16, b);
 }
 
+// k_h of batch element b as a float (exact: it is an fp16 value)
+__device__ inline float head_factor(const Factors& f, int b, int H, int h) {
+  return half_bits_to_float(f.kh_bh ? f.kh_bh[b * H + h] : f.kh.bits[h]);
+}
+
 // ---------------------------------------------------------------- K1
 
 // Thread i handles 8 consecutive d (16 bytes) of one (row, head): reads are
@@ -91,9 +97,10 @@ __device__ inline float half_bits_to_float(uint16_t b) {
 template <int MODE, bool FP8>
 __global__ __launch_bounds__(256) void scale_queries_kernel(
     const f16x8* __restrict__ q, const _Float16* __restrict__ gate, int H, int64_t rows_in,
-    int64_t rows_valid, int64_t rows_out, HeadFactors kh, const float* __restrict__ inv_q,
-    void* __restrict__ out) {
+    int64_t rows_valid_all, const int64_t* __restrict__ rows_valid_b, int64_t rows_out, Factors f,
+    const float* __restrict__ inv_q, void* __restrict__ out) {
   const int b = blockIdx.y;
+  const int64_t rows_valid = rows_valid_b ? rows_valid_b[b] : rows_valid_all;
   const int64_t per_row = (int64_t)H * 8;
   const int64_t items = rows_out * per_row;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < items;
@@ -104,7 +111,7 @@ __global__ __launch_bounds__(256) void scale_queries_kernel(
     f16x8 y = {};
     if (row < rows_valid) {
       const f16x8 x = q[((int64_t)b * rows_in + row) * per_row + cg];
-      const float k = half_bits_to_float(kh.bits[h]);
+      const float k = head_factor(f, b, H, h);
       float u = 1.0f;
       if constexpr (MODE == kScaleGated) u = gate_factor(gate[((int64_t)b * rows_in + row) * H + h]);
 #pragma unroll
@@ -131,15 +138,16 @@ __global__ __launch_bounds__(256) void scale_queries_kernel(
 template <int MODE>
 __global__ void amax_kernel(const f16x8* __restrict__ q, const f16x8* __restrict__ k,
                             const f16x8* __restrict__ v, const _Float16* __restrict__ gate,
-                            int H, int64_t rows_padded, int64_t n, int rows_per_block,
-                            HeadFactors kh, uint32_t* __restrict__ amax_bits) {
+                            int H, int64_t rows_padded, const int64_t* __restrict__ n_b,
+                            int rows_per_block, Factors f, uint32_t* __restrict__ amax_bits) {
   extern __shared__ float red[];  // [3][blockDim.x]
   const int b = blockIdx.y;
+  const int64_t n = n_b[b];
   const int per_row = H * 8;
   const int t = threadIdx.x;
   const int cg = t % per_row, roff = t / per_row, rstep = blockDim.x / per_row;
   const int h = cg >> 3;
-  const float kf = half_bits_to_float(kh.bits[h]);
+  const float kf = head_factor(f, b, H, h);
   float mq = 0.f, mk = 0.f, mv = 0.f;
   const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
   const int64_t r1 = min(n, r0 + rows_per_block);
@@ -199,12 +207,13 @@ __global__ void scales_kernel(const uint32_t* __restrict__ amax_bits, int count,
 template <bool FP8>
 __global__ __launch_bounds__(256) void pack_kv_kernel(
     const f16x8* __restrict__ k, const f16x8* __restrict__ v, int H, int64_t rows_padded,
-    int64_t n, int64_t n_alloc, const float* __restrict__ inv_k, const float* __restrict__ inv_v,
-    void* __restrict__ kc, void* __restrict__ vt) {
+    const int64_t* __restrict__ n_b, int64_t n_alloc, const float* __restrict__ inv_k,
+    const float* __restrict__ inv_v, void* __restrict__ kc, void* __restrict__ vt) {
   constexpr int EB = FP8 ? 1 : 2;
   __shared__ __attribute__((aligned(16))) unsigned char vs[64 * (64 * EB + 16)];
   constexpr int VSROW = 64 * EB + 16;
   const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int64_t n = n_b[b];
   const int bh = b * H + h;
   const int t = threadIdx.x;
   const int row = t >> 2, quarter = t & 3;   // 16 d per thread
@@ -266,34 +275,34 @@ hipError_t launch_fill_f32(float* p, int64_t count, float value, hipStream_t s) 
 }
 
 hipError_t launch_fp8_scales(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                             const uint16_t* gate, int B, int64_t rows_padded, int64_t n,
-                             int H, int mode, const HeadFactors& kh, uint32_t* amax_bits,
-                             float* scales, float* inv, hipStream_t s) {
+                             const uint16_t* gate, int B, int64_t rows_padded, int64_t n_max,
+                             const int64_t* n_b, int H, int mode, const Factors& f,
+                             uint32_t* amax_bits, float* scales, float* inv, hipStream_t s) {
   const int count = 3 * B * H;
   hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(256), 0, s, amax_bits, (int64_t)count, 0u);
   const int per_row = H * 8;
   const int kmul = per_row >= 256 ? 1 : 256 / per_row;
   const int block = per_row * kmul;
   const int rows_per_block = 512;
-  const dim3 grid((unsigned)((n + rows_per_block - 1) / rows_per_block), (unsigned)B);
+  const dim3 grid((unsigned)((n_max + rows_per_block - 1) / rows_per_block), (unsigned)B);
   const size_t lds = 3 * (size_t)block * sizeof(float);
   auto qv = reinterpret_cast<const f16x8*>(q);
   auto kv = reinterpret_cast<const f16x8*>(k);
   auto vv = reinterpret_cast<const f16x8*>(v);
   auto gv = reinterpret_cast<const _Float16*>(gate);
   if (mode == kScaleNone)
-    hipLaunchKernelGGL(amax_kernel<kScaleNone>, grid, dim3(block), lds, s, qv, kv, vv, gv, H, rows_padded, n, rows_per_block, kh, amax_bits);
+    hipLaunchKernelGGL(amax_kernel<kScaleNone>, grid, dim3(block), lds, s, qv, kv, vv, gv, H, rows_padded, n_b, rows_per_block, f, amax_bits);
   else if (mode == kScaleLog)
-    hipLaunchKernelGGL(amax_kernel<kScaleLog>, grid, dim3(block), lds, s, qv, kv, vv, gv, H, rows_padded, n, rows_per_block, kh, amax_bits);
+    hipLaunchKernelGGL(amax_kernel<kScaleLog>, grid, dim3(block), lds, s, qv, kv, vv, gv, H, rows_padded, n_b, rows_per_block, f, amax_bits);
   else
-    hipLaunchKernelGGL(amax_kernel<kScaleGated>, grid, dim3(block), lds, s, qv, kv, vv, gv, H, rows_padded, n, rows_per_block, kh, amax_bits);
+    hipLaunchKernelGGL(amax_kernel<kScaleGated>, grid, dim3(block), lds, s, qv, kv, vv, gv, H, rows_padded, n_b, rows_per_block, f, amax_bits);
   hipLaunchKernelGGL(scales_kernel, dim3((count + 255) / 256), dim3(256), 0, s, amax_bits, count, scales, inv);
   return hipGetLastError();
 }
 
 hipError_t launch_scale_queries(const uint16_t* q, const uint16_t* gate, int B, int64_t rows_in,
-                                int64_t rows_valid, int64_t rows_out, int H, int mode,
-                                const HeadFactors& kh, const float* inv_q, void* out,
+                                int64_t rows_valid, const int64_t* rows_valid_b, int64_t rows_out,
+                                int H, int mode, const Factors& f, const float* inv_q, void* out,
                                 hipStream_t s) {
   const int64_t items = rows_out * H * 8;
   const dim3 grid((unsigned)grid_for(items, 256, 4096), (unsigned)B);
@@ -301,7 +310,7 @@ hipError_t launch_scale_queries(const uint16_t* q, const uint16_t* gate, int B, 
   auto gv = reinterpret_cast<const _Float16*>(gate);
 #define SDM_K1(MODE, FP8)                                                                     \
   hipLaunchKernelGGL((scale_queries_kernel<MODE, FP8>), grid, dim3(256), 0, s, qv, gv, H,      \
-                     rows_in, rows_valid, rows_out, kh, inv_q, out)
+                     rows_in, rows_valid, rows_valid_b, rows_out, f, inv_q, out)
   const bool fp8 = inv_q != nullptr;
   if (mode == kScaleNone) { if (fp8) SDM_K1(kScaleNone, true); else SDM_K1(kScaleNone, false); }
   else if (mode == kScaleLog) { if (fp8) SDM_K1(kScaleLog, true); else SDM_K1(kScaleLog, false); }
@@ -311,15 +320,15 @@ hipError_t launch_scale_queries(const uint16_t* q, const uint16_t* gate, int B, 
 }
 
 hipError_t launch_pack_kv(const uint16_t* k, const uint16_t* v, int B, int64_t rows_padded,
-                          int64_t n, int64_t n_alloc, int H, int prec, const float* inv_k,
+                          const int64_t* n_b, int64_t n_alloc, int H, int prec, const float* inv_k,
                           const float* inv_v, void* kc, void* vt, hipStream_t s) {
   const dim3 grid((unsigned)(n_alloc / 64), (unsigned)H, (unsigned)B);
   auto kv = reinterpret_cast<const f16x8*>(k);
   auto vv = reinterpret_cast<const f16x8*>(v);
   if (prec == kPrecFp8)
-    hipLaunchKernelGGL(pack_kv_kernel<true>, grid, dim3(256), 0, s, kv, vv, H, rows_padded, n, n_alloc, inv_k, inv_v, kc, vt);
+    hipLaunchKernelGGL(pack_kv_kernel<true>, grid, dim3(256), 0, s, kv, vv, H, rows_padded, n_b, n_alloc, inv_k, inv_v, kc, vt);
   else
-    hipLaunchKernelGGL(pack_kv_kernel<false>, grid, dim3(256), 0, s, kv, vv, H, rows_padded, n, n_alloc, inv_k, inv_v, kc, vt);
+    hipLaunchKernelGGL(pack_kv_kernel<false>, grid, dim3(256), 0, s, kv, vv, H, rows_padded, n_b, n_alloc, inv_k, inv_v, kc, vt);
   return hipGetLastError();
 }
 

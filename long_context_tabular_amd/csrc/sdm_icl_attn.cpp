@@ -27,14 +27,17 @@ struct sdm_icl_cache_s {
   int device;
   hipStream_t stream;
   int32_t B, H, D, prec, mode, splits;
-  int64_t n, n_alloc, tiles_per_split;
-  float L32;
-  HeadFactors kh;
-  void* block;     // one device allocation: [kc][vt][scales 3BH][inv 3BH]
+  int64_t n_max, n_alloc, tiles_per_split;
+  std::vector<int64_t> lengths;   // n_b
+  std::vector<float> L32;         // L32 of each batch element
+  std::vector<uint16_t> kh;       // fp16 bits of k_h per (b, h) ([B*H], empty for NONE)
+  void* block;     // one device allocation: [kc][vt][scales 3BH][inv 3BH][n_b B][k_h BH]
   void* kc;
   void* vt;
   float* scales;
   float* inv;
+  int64_t* n_dev;
+  uint16_t* kh_dev;
   size_t bytes;
 };
 
@@ -233,7 +236,7 @@ AttnArgs attn_args(const sdm_icl_cache_s* c) {
   a.kc = c->kc;
   a.vt = c->vt;
   a.scales = c->scales;
-  a.n = c->n;
+  a.n_b = c->n_dev;
   a.n_alloc = c->n_alloc;
   a.heads = c->H;
   a.bh_count = c->B * c->H;
@@ -245,7 +248,7 @@ AttnArgs attn_args(const sdm_icl_cache_s* c) {
 
 extern "C" {
 
-int32_t sdm_icl_version(void) { return 100; }
+int32_t sdm_icl_version(void) { return 101; }
 
 const char* sdm_icl_last_error(void) { return g_error.c_str(); }
 
@@ -282,11 +285,13 @@ sdm_icl_status sdm_icl_attn_fit(const sdm_icl_fit_args* a, sdm_icl_cache* out) {
   if (a->heads > kMaxHeads) return fail(SDM_ICL_E_UNSUPPORTED, "fit: at most %d heads", kMaxHeads);
   if (a->head_dim != kHeadDim) return fail(SDM_ICL_E_UNSUPPORTED, "fit: head_dim must be 64 (got %d)", a->head_dim);
   if (!a->lengths) return fail(SDM_ICL_E_INVALID, "fit: lengths is NULL");
-  const int64_t n = a->lengths[0];
-  for (int b = 1; b < a->batch; ++b)
-    if (a->lengths[b] != n)
-      return fail(SDM_ICL_E_UNSUPPORTED, "fit: per-batch lengths differ (only a shared length is supported)");
-  if (n < 1 || n > a->rows_padded) return fail(SDM_ICL_E_INVALID, "fit: need 1 <= n <= rows_padded (n=%lld)", (long long)n);
+  int64_t n = 0;  // the longest context of the batch
+  for (int b = 0; b < a->batch; ++b) {
+    const int64_t nb = a->lengths[b];
+    if (nb < 1 || nb > a->rows_padded)
+      return fail(SDM_ICL_E_INVALID, "fit: need 1 <= lengths[%d] <= rows_padded (got %lld)", b, (long long)nb);
+    if (nb > n) n = nb;
+  }
   if (!a->q || !a->k || !a->v) return fail(SDM_ICL_E_INVALID, "fit: q, k and v are required");
   if (a->scale_mode < SDM_ICL_SCALE_NONE || a->scale_mode > SDM_ICL_SCALE_GATED_LOG)
     return fail(SDM_ICL_E_INVALID, "fit: unknown scale_mode %d", a->scale_mode);
@@ -327,22 +332,43 @@ sdm_icl_status sdm_icl_attn_fit(const sdm_icl_fit_args* a, sdm_icl_cache* out) {
   c->B = B; c->H = H; c->D = kHeadDim;
   c->prec = prec;
   c->mode = a->scale_mode;
-  c->n = n;
+  c->n_max = n;
   c->n_alloc = round_up(n, kKeyTile);
-  c->L32 = length_scalar(n);
-  if (a->scale_mode != SDM_ICL_SCALE_NONE) head_factors(n, a->head_coef, H, &c->kh);
-  else std::memset(&c->kh, 0, sizeof c->kh);
+  c->lengths.assign(a->lengths, a->lengths + B);
+  c->L32.resize(B);
+  c->kh.assign((size_t)B * H, 0);
+  for (int b = 0; b < B; ++b) {
+    c->L32[b] = length_scalar(c->lengths[b]);
+    if (a->scale_mode != SDM_ICL_SCALE_NONE) {
+      HeadFactors f;
+      head_factors(c->lengths[b], a->head_coef, H, &f);
+      std::memcpy(&c->kh[(size_t)b * H], f.bits, sizeof(uint16_t) * H);
+    }
+  }
   plan_splits(n, di.cus, (int64_t)B * H, &c->splits, &c->tiles_per_split);
 
   const size_t kv_bytes = (size_t)B * H * c->n_alloc * kHeadDim * eb;
   const size_t sc_bytes = (size_t)6 * B * H * sizeof(float);
-  c->bytes = 2 * kv_bytes + sc_bytes;
+  const size_t len_bytes = (size_t)B * sizeof(int64_t);
+  const size_t kh_bytes = (size_t)B * H * sizeof(uint16_t);
+  c->bytes = 2 * kv_bytes + sc_bytes + len_bytes + kh_bytes;
   hipError_t e = hipMallocAsync(&c->block, c->bytes, s);
   if (e != hipSuccess) { delete c; return hip_fail(e, "fit: cache allocation"); }
   c->kc = c->block;
   c->vt = (char*)c->block + kv_bytes;
   c->scales = (float*)((char*)c->block + 2 * kv_bytes);
   c->inv = c->scales + 3 * B * H;
+  c->n_dev = (int64_t*)((char*)c->block + 2 * kv_bytes + sc_bytes);  // 8-byte aligned: 24BH bytes of scales
+  c->kh_dev = (uint16_t*)((char*)c->n_dev + len_bytes);
+  // the host copies live as long as the cache, so the source outlives the copy
+  e = hipMemcpyAsync(c->n_dev, c->lengths.data(), len_bytes, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(c->kh_dev, c->kh.data(), kh_bytes, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) {
+    (void)hipFreeAsync(c->block, s);
+    delete c;
+    return hip_fail(e, "fit: length upload");
+  }
+  const Factors fac{c->kh_dev, HeadFactors{}};
 
   // temporaries: amax scratch and the context Q operand
   const int64_t q_rows_alloc = round_up(n, kQueryPad);
@@ -366,27 +392,28 @@ sdm_icl_status sdm_icl_attn_fit(const sdm_icl_fit_args* a, sdm_icl_cache* out) {
 
   if (prec == SDM_ICL_PREC_FP8_E4M3) {
     TimedLaunch tl(SDM_ICL_TIMING_PREP, s);
-    e = launch_fp8_scales(q16, k16, v16, g16, B, a->rows_padded, n, H, a->scale_mode, c->kh, amax,
-                          c->scales, c->inv, s);
+    e = launch_fp8_scales(q16, k16, v16, g16, B, a->rows_padded, n, c->n_dev, H, a->scale_mode, fac,
+                          amax, c->scales, c->inv, s);
   } else {
     e = launch_fill_f32(c->scales, 6 * (int64_t)B * H, 1.0f, s);
   }
   if (e == hipSuccess) {
     TimedLaunch tl(SDM_ICL_TIMING_PREP, s);
-    e = launch_pack_kv(k16, v16, B, a->rows_padded, n, c->n_alloc, H, prec, c->inv + B * H,
+    e = launch_pack_kv(k16, v16, B, a->rows_padded, c->n_dev, c->n_alloc, H, prec, c->inv + B * H,
                        c->inv + 2 * B * H, c->kc, c->vt, s);
   }
   if (e == hipSuccess && a->out_ctx) {
     {
       TimedLaunch tl(SDM_ICL_TIMING_SCALE, s);
-      e = launch_scale_queries(q16, g16, B, a->rows_padded, n, q_rows_alloc, H, a->scale_mode, c->kh,
-                               prec == SDM_ICL_PREC_FP8_E4M3 ? c->inv : nullptr, qctx, s);
+      e = launch_scale_queries(q16, g16, B, a->rows_padded, n, c->n_dev, q_rows_alloc, H, a->scale_mode,
+                               fac, prec == SDM_ICL_PREC_FP8_E4M3 ? c->inv : nullptr, qctx, s);
     }
     if (e == hipSuccess) {
       AttnArgs at = attn_args(c);
       at.q = qctx;
       at.q_rows_alloc = q_rows_alloc;
       at.q_rows_valid = n;
+      at.ctx = 1;
       at.out_rows = a->rows_padded;
       at.out = (uint16_t*)a->out_ctx;
       at.splits = 1;
@@ -453,8 +480,9 @@ sdm_icl_status sdm_icl_attn_query(sdm_icl_cache c, const void* q, const void* ga
   hipError_t e;
   {
     TimedLaunch tl(SDM_ICL_TIMING_SCALE, s);
-    e = launch_scale_queries((const uint16_t*)q, (const uint16_t*)gate, c->B, R, R, L.q_rows_alloc,
-                             c->H, c->mode, c->kh,
+    const Factors fac{c->kh_dev, HeadFactors{}};
+    e = launch_scale_queries((const uint16_t*)q, (const uint16_t*)gate, c->B, R, R, nullptr,
+                             L.q_rows_alloc, c->H, c->mode, fac,
                              c->prec == SDM_ICL_PREC_FP8_E4M3 ? c->inv : nullptr, qbuf, s);
   }
   if (e != hipSuccess) return hip_fail(e, "query: scale launch");
@@ -495,10 +523,10 @@ sdm_icl_status sdm_icl_attn_cache_info(sdm_icl_cache c, sdm_icl_cache_info* info
   info->precision = c->prec;
   info->scale_mode = c->mode;
   info->kv_splits = c->splits;
-  info->n_valid = c->n;
+  info->n_valid = c->n_max;
   info->rows_alloc = c->n_alloc;
   info->keys_per_split = c->tiles_per_split * kKeyTile;
-  info->length_scalar = c->L32;
+  info->length_scalar = c->L32[0];
   info->device_bytes = c->bytes;
   return SDM_ICL_OK;
 }
@@ -518,8 +546,8 @@ sdm_icl_status sdm_icl_attn_cache_export(sdm_icl_cache c, void* host_k, void* ho
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return hip_fail(e, "cache_export: K copy");
     for (int64_t bh = 0; bh < BH; ++bh)
-      std::memcpy((char*)host_k + bh * c->n * row_bytes, tmp.data() + bh * c->n_alloc * row_bytes,
-                  (size_t)(c->n * row_bytes));
+      std::memcpy((char*)host_k + bh * c->n_max * row_bytes, tmp.data() + bh * c->n_alloc * row_bytes,
+                  (size_t)(c->n_max * row_bytes));
   }
   if (host_v) {
     e = hipMemcpyAsync(tmp.data(), c->vt, kv_bytes, hipMemcpyDeviceToHost, s);
@@ -532,8 +560,8 @@ sdm_icl_status sdm_icl_attn_cache_export(sdm_icl_cache c, void* host_k, void* ho
         for (int d = 0; d < kHeadDim; ++d)
           for (int j = 0; j < kKeyTile; ++j) {
             const int64_t key = t * kKeyTile + j;
-            if (key >= c->n) break;
-            std::memcpy((char*)host_v + ((bh * c->n + key) * kHeadDim + d) * eb,
+            if (key >= c->n_max) break;
+            std::memcpy((char*)host_v + ((bh * c->n_max + key) * kHeadDim + d) * eb,
                         tmp.data() + (((bh * tiles + t) * kHeadDim + d) * kKeyTile + j) * eb, (size_t)eb);
           }
   }
@@ -542,6 +570,14 @@ sdm_icl_status sdm_icl_attn_cache_export(sdm_icl_cache c, void* host_k, void* ho
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) return hip_fail(e, "cache_export: scales copy");
   }
+  return SDM_ICL_OK;
+}
+
+sdm_icl_status sdm_icl_attn_cache_lengths(sdm_icl_cache c, int64_t* host_lengths,
+                                          float* host_length_scalars) {
+  if (!live(c)) return fail(SDM_ICL_E_STATE, "cache_lengths: unknown or released cache");
+  if (host_lengths) std::memcpy(host_lengths, c->lengths.data(), sizeof(int64_t) * c->B);
+  if (host_length_scalars) std::memcpy(host_length_scalars, c->L32.data(), sizeof(float) * c->B);
   return SDM_ICL_OK;
 }
 
@@ -623,8 +659,9 @@ sdm_icl_status sdm_icl_log_scale(const void* q, const void* gate, int32_t batch,
   if (scale_mode != SDM_ICL_SCALE_NONE) head_factors(key_length, head_coef, heads, &kh);
   else std::memset(&kh, 0, sizeof kh);
   TimedLaunch tl(SDM_ICL_TIMING_SCALE, (hipStream_t)stream);
-  hipError_t e = launch_scale_queries((const uint16_t*)q, (const uint16_t*)gate, batch, rows, rows, rows,
-                                      heads, scale_mode, kh, q_inv_scale, out, (hipStream_t)stream);
+  const Factors fac{nullptr, kh};
+  hipError_t e = launch_scale_queries((const uint16_t*)q, (const uint16_t*)gate, batch, rows, rows, nullptr,
+                                      rows, heads, scale_mode, fac, q_inv_scale, out, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "log_scale: launch");
   return SDM_ICL_OK;
 }

@@ -56,7 +56,7 @@ class Run:
     def oracle(self) -> icl.OracleCache:
         if self._oracle is None:
             x, w = self.x, self.w
-            self._oracle = icl.fit(x.q_ctx, x.k_ctx, x.v_ctx, w.n_valid, w.scale_mode, w.precision,
+            self._oracle = icl.fit(x.q_ctx, x.k_ctx, x.v_ctx, w.length_list(), w.scale_mode, w.precision,
                                    self.coef, x.gate_ctx if self.gate is not None else None,
                                    keep_codes=self._oracle_codes)
         return self._oracle
@@ -66,7 +66,7 @@ class Run:
         out = torch.empty_like(self.q) if out_ctx else None
         if out is not None:
             out.fill_(float("nan"))
-        cache = B.sdm_icl_attn_fit(self.q, self.k, self.v, self.w.n_valid, self.w.scale_mode,
+        cache = B.sdm_icl_attn_fit(self.q, self.k, self.v, self.w.length_list(), self.w.scale_mode,
                                    self.w.precision, self.coef, self.gate, out)
         return cache, out
 
@@ -77,11 +77,11 @@ class Run:
             g = self.gq if rows is None else self.gq[:, rows[0]:rows[1]].contiguous()
         return B.sdm_icl_attn_query(cache, q, g)
 
-    def ref_context(self, rows, heads=None) -> np.ndarray:
+    def ref_context(self, rows, heads=None, b: int = 0) -> np.ndarray:
         gate = self.x.gate_ctx if self.gate is not None else None
-        return icl.context_outputs(self.oracle, self.x.q_ctx, gate, rows, heads=heads)
+        return icl.context_outputs(self.oracle, self.x.q_ctx, gate, rows, b=b, heads=heads)
 
-    def ref_query(self, rows, heads=None) -> np.ndarray:
+    def ref_query(self, rows, heads=None, b: int = 0) -> np.ndarray:
         rows = np.asarray(rows)
-        gate = self.x.gate_query[0, rows] if self.gq is not None else None
-        return icl.attend(self.oracle, self.x.q_query[0, rows], gate, heads=heads)
+        gate = self.x.gate_query[b, rows] if self.gq is not None else None
+        return icl.attend(self.oracle, self.x.q_query[b, rows], gate, b=b, heads=heads)
