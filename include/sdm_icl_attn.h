@@ -74,6 +74,18 @@ typedef int32_t sdm_icl_status;
 #define SDM_ICL_PREC_FP16     0
 #define SDM_ICL_PREC_FP8_E4M3 1
 #define SDM_ICL_PREC_AUTO     2  /* FP8 iff n > 8192 valid context rows ("[FP8 3/4] ...", intro) */
+#define SDM_ICL_PREC_SCOPED   3  /* an intermediate ICL layer under the opt-in FP8 scope: FP8 iff
+                                    the calling thread's scope enables FP8 and n > 8192, else
+                                    FP16 (see sdm_icl_scope_push); a final layer asks for FP16 */
+
+/* Settings of an FP8 scope ("[FP8 3/4] ...", introduction and API example:
+ * sdm.optimize(attention="fp8") is an opt-in scope that enables, disables or
+ * inherits FP8 attention; using an FP8 cache outside the enabled scope is an
+ * error and re-entering permits reuse; leaving a scope restores the previous
+ * setting without touching caches). */
+#define SDM_ICL_SCOPE_DISABLE 0
+#define SDM_ICL_SCOPE_ENABLE  1
+#define SDM_ICL_SCOPE_INHERIT 2
 
 /* Opaque, library-owned, immutable after fit.  Holds n, the scaling factors,
  * the per-head FP8 scales and the K/V operands in a head-major layout. */
@@ -218,6 +230,24 @@ int32_t sdm_icl_select_precision(int64_t n, int32_t requested);
  * shorter element's n_b hold no keys of it and weigh 0 in its combine. */
 sdm_icl_status sdm_icl_split_plan(int64_t n, int32_t num_cus, int32_t bh_count, int32_t* kv_splits,
                                   int64_t* keys_per_split);
+
+/* Open a nested FP8 scope on the calling thread with one of the
+ * SDM_ICL_SCOPE_* settings (INHERIT keeps the enclosing setting).  The
+ * effective setting is that of the innermost scope that is not INHERIT,
+ * disabled when there is none; a new thread starts with no scope.  It decides
+ * SDM_ICL_PREC_SCOPED at fit, and a cache that resolved to FP8 that way can
+ * only be queried or exported while the effective setting is ENABLE
+ * (SDM_ICL_E_STATE otherwise); closing the scope changes no cache.  At most
+ * 256 nested scopes (SDM_ICL_E_STATE beyond); an unknown setting is
+ * SDM_ICL_E_INVALID. */
+sdm_icl_status sdm_icl_scope_push(int32_t setting);
+
+/* Close the innermost scope of the calling thread (SDM_ICL_E_STATE if none is
+ * open). */
+sdm_icl_status sdm_icl_scope_pop(void);
+
+/* 1 if the calling thread's effective FP8 scope setting is ENABLE, else 0. */
+int32_t sdm_icl_scope_fp8(void);
 
 /* Message of the last non-OK status on this thread ("" if none). */
 const char* sdm_icl_last_error(void);

@@ -10,6 +10,8 @@ streams only.
 """
 from __future__ import annotations
 
+import contextlib
+import contextvars
 import ctypes
 import os
 from typing import Optional
@@ -23,7 +25,8 @@ SDM_ICL_OK = 0
 STATUS_NAMES = {0: "OK", 1: "E_INVALID", 2: "E_UNSUPPORTED", 3: "E_DEVICE", 4: "E_OOM",
                 5: "E_HIP", 6: "E_STATE"}
 SDM_ICL_SCALE_NONE, SDM_ICL_SCALE_LOG, SDM_ICL_SCALE_GATED_LOG = 0, 1, 2
-SDM_ICL_PREC_FP16, SDM_ICL_PREC_FP8_E4M3, SDM_ICL_PREC_AUTO = 0, 1, 2
+SDM_ICL_PREC_FP16, SDM_ICL_PREC_FP8_E4M3, SDM_ICL_PREC_AUTO, SDM_ICL_PREC_SCOPED = 0, 1, 2, 3
+SDM_ICL_SCOPE_DISABLE, SDM_ICL_SCOPE_ENABLE, SDM_ICL_SCOPE_INHERIT = 0, 1, 2
 
 
 class SdmIclError(RuntimeError):
@@ -78,6 +81,9 @@ _SIGNATURES = {
     "sdm_icl_select_precision": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32]),
     "sdm_icl_split_plan": (ctypes.c_int32, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                             ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]),
+    "sdm_icl_scope_push": (ctypes.c_int32, [ctypes.c_int32]),
+    "sdm_icl_scope_pop": (ctypes.c_int32, []),
+    "sdm_icl_scope_fp8": (ctypes.c_int32, []),
     "sdm_icl_last_error": (ctypes.c_char_p, []),
     "sdm_icl_version": (ctypes.c_int32, []),
 }
@@ -103,6 +109,50 @@ def lib() -> ctypes.CDLL:
 def _check(status: int) -> None:
     if status != SDM_ICL_OK:
         raise SdmIclError(status, lib().sdm_icl_last_error().decode())
+
+
+# The FP8 scope of the Python caller, context-local (threads and asyncio tasks
+# each see their own), as the settings of the pages' optimize scope are.  The
+# library keeps its scope per OS thread, so every call that depends on it
+# pushes this context's effective setting around the C call.
+_SCOPE: contextvars.ContextVar = contextvars.ContextVar("sdm_icl_fp8_scope", default=())
+
+
+def _effective_scope() -> int:
+    for setting in reversed(_SCOPE.get()):
+        if setting != SDM_ICL_SCOPE_INHERIT:
+            return setting
+    return SDM_ICL_SCOPE_DISABLE
+
+
+@contextlib.contextmanager
+def optimize(attention: Optional[str] = "fp8"):
+    """Opt-in FP8 attention scope: ``attention="fp8"`` enables FP8 for
+    intermediate layers (fits with ``SDM_ICL_PREC_SCOPED``), ``"none"``
+    disables it, ``None`` inherits the enclosing setting.  Leaving the scope
+    restores the previous setting and leaves caches untouched."""
+    setting = {"fp8": SDM_ICL_SCOPE_ENABLE, "none": SDM_ICL_SCOPE_DISABLE,
+               None: SDM_ICL_SCOPE_INHERIT}.get(attention)
+    if setting is None and attention is not None:
+        raise ValueError(f"unknown attention optimisation {attention!r}")
+    token = _SCOPE.set(_SCOPE.get() + (setting,))
+    try:
+        yield
+    finally:
+        _SCOPE.reset(token)
+
+
+def fp8_scope_enabled() -> bool:
+    return _effective_scope() == SDM_ICL_SCOPE_ENABLE
+
+
+@contextlib.contextmanager
+def _c_scope():
+    _check(lib().sdm_icl_scope_push(_effective_scope()))
+    try:
+        yield
+    finally:
+        _check(lib().sdm_icl_scope_pop())
 
 
 def _stream_ptr(stream) -> Optional[int]:
@@ -144,6 +194,18 @@ def sdm_icl_head_factors(n: int, head_coef) -> np.ndarray:
     _check(lib().sdm_icl_head_factors(int(n), coef.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
                                       coef.size, out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint16))))
     return out.view(np.float16)
+
+
+def sdm_icl_scope_push(setting: int) -> None:
+    _check(lib().sdm_icl_scope_push(int(setting)))
+
+
+def sdm_icl_scope_pop() -> None:
+    _check(lib().sdm_icl_scope_pop())
+
+
+def sdm_icl_scope_fp8() -> int:
+    return lib().sdm_icl_scope_fp8()
 
 
 def sdm_icl_select_precision(n: int, requested: int) -> int:
@@ -232,7 +294,8 @@ def sdm_icl_attn_fit(q, k, v, length, scale_mode: int = SDM_ICL_SCALE_NONE,
                    precision=precision, out_ctx=_dev_ptr(out_ctx, "out_ctx", f16),
                    stream=_stream_ptr(stream))
     handle = ctypes.c_void_p()
-    _check(lib().sdm_icl_attn_fit(ctypes.byref(args), ctypes.byref(handle)))
+    with _c_scope():
+        _check(lib().sdm_icl_attn_fit(ctypes.byref(args), ctypes.byref(handle)))
     return Cache(handle.value)
 
 
@@ -256,10 +319,11 @@ def sdm_icl_attn_query(cache: Cache, q, gate=None, out=None, workspace=None, str
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
-    _check(lib().sdm_icl_attn_query(cache.handle, _dev_ptr(q, "q", torch.float16),
-                                    _dev_ptr(gate, "gate", torch.float16), R,
-                                    _dev_ptr(out, "out", torch.float16),
-                                    _dev_ptr(workspace, "workspace"), ws_bytes, _stream_ptr(stream)))
+    with _c_scope():
+        _check(lib().sdm_icl_attn_query(cache.handle, _dev_ptr(q, "q", torch.float16),
+                                        _dev_ptr(gate, "gate", torch.float16), R,
+                                        _dev_ptr(out, "out", torch.float16),
+                                        _dev_ptr(workspace, "workspace"), ws_bytes, _stream_ptr(stream)))
     return out
 
 
@@ -278,8 +342,9 @@ def sdm_icl_attn_cache_export(cache: Cache, stream=None):
     k = np.empty(shape, dtype=dt)
     v = np.empty(shape, dtype=dt)
     sc = np.empty((3, i["batch"], i["heads"]), dtype=np.float32)
-    _check(lib().sdm_icl_attn_cache_export(cache.handle, k.ctypes.data, v.ctypes.data,
-                                           sc.ctypes.data, _stream_ptr(stream)))
+    with _c_scope():
+        _check(lib().sdm_icl_attn_cache_export(cache.handle, k.ctypes.data, v.ctypes.data,
+                                               sc.ctypes.data, _stream_ptr(stream)))
     return k, v, sc
 
 

@@ -28,6 +28,7 @@ struct sdm_icl_cache_s {
   hipStream_t stream;
   int32_t B, H, D, prec, mode, splits;
   int64_t n_max, n_alloc, tiles_per_split;
+  bool scoped;                    // FP8 chosen by the FP8 scope: usable only inside an enabled scope
   std::vector<int64_t> lengths;   // n_b
   std::vector<float> L32;         // L32 of each batch element
   std::vector<uint16_t> kh;       // fp16 bits of k_h per (b, h) ([B*H], empty for NONE)
@@ -106,8 +107,22 @@ void head_factors(int64_t n, const float* coef, int H, HeadFactors* out) {
     out->bits[h] = h < H ? f32_to_f16_bits(L * coef[h]) : (uint16_t)0;
 }
 
+// ---- opt-in FP8 scope: a per-thread stack of settings (enable / disable /
+// inherit); the effective setting is the innermost one that is not inherit,
+// disabled when there is none
+constexpr size_t kMaxScopeDepth = 256;
+thread_local std::vector<int8_t> g_scope;
+
+bool scope_fp8() {
+  for (auto it = g_scope.rbegin(); it != g_scope.rend(); ++it)
+    if (*it != SDM_ICL_SCOPE_INHERIT) return *it == SDM_ICL_SCOPE_ENABLE;
+  return false;
+}
+
 int32_t resolve_precision(int64_t n, int32_t requested) {
   if (requested == SDM_ICL_PREC_AUTO) return n > kFp8MinRows ? SDM_ICL_PREC_FP8_E4M3 : SDM_ICL_PREC_FP16;
+  if (requested == SDM_ICL_PREC_SCOPED)
+    return scope_fp8() && n > kFp8MinRows ? SDM_ICL_PREC_FP8_E4M3 : SDM_ICL_PREC_FP16;
   return requested;
 }
 
@@ -266,6 +281,22 @@ sdm_icl_status sdm_icl_head_factors(int64_t n, const float* head_coef, int32_t h
 
 int32_t sdm_icl_select_precision(int64_t n, int32_t requested) { return resolve_precision(n, requested); }
 
+sdm_icl_status sdm_icl_scope_push(int32_t setting) {
+  if (setting != SDM_ICL_SCOPE_DISABLE && setting != SDM_ICL_SCOPE_ENABLE && setting != SDM_ICL_SCOPE_INHERIT)
+    return fail(SDM_ICL_E_INVALID, "scope_push: unknown setting %d", setting);
+  if (g_scope.size() >= kMaxScopeDepth) return fail(SDM_ICL_E_STATE, "scope_push: more than %zu nested scopes", kMaxScopeDepth);
+  g_scope.push_back((int8_t)setting);
+  return SDM_ICL_OK;
+}
+
+sdm_icl_status sdm_icl_scope_pop(void) {
+  if (g_scope.empty()) return fail(SDM_ICL_E_STATE, "scope_pop: no scope is open on this thread");
+  g_scope.pop_back();
+  return SDM_ICL_OK;
+}
+
+int32_t sdm_icl_scope_fp8(void) { return scope_fp8() ? 1 : 0; }
+
 sdm_icl_status sdm_icl_split_plan(int64_t n, int32_t num_cus, int32_t bh_count, int32_t* kv_splits,
                                   int64_t* keys_per_split) {
   if (!kv_splits || !keys_per_split) return fail(SDM_ICL_E_INVALID, "split_plan: null pointer");
@@ -299,7 +330,7 @@ sdm_icl_status sdm_icl_attn_fit(const sdm_icl_fit_args* a, sdm_icl_cache* out) {
     return fail(SDM_ICL_E_INVALID, "fit: gate must be given exactly when scale_mode is GATED_LOG");
   if ((a->head_coef != nullptr) != (a->scale_mode != SDM_ICL_SCALE_NONE))
     return fail(SDM_ICL_E_INVALID, "fit: head_coef must be given exactly when scale_mode is LOG or GATED_LOG");
-  if (a->precision < SDM_ICL_PREC_FP16 || a->precision > SDM_ICL_PREC_AUTO)
+  if (a->precision < SDM_ICL_PREC_FP16 || a->precision > SDM_ICL_PREC_SCOPED)
     return fail(SDM_ICL_E_INVALID, "fit: unknown precision %d", a->precision);
   if ((int64_t)a->batch * a->rows_padded * a->heads > (int64_t)1 << 40)
     return fail(SDM_ICL_E_INVALID, "fit: problem too large");
@@ -332,6 +363,7 @@ sdm_icl_status sdm_icl_attn_fit(const sdm_icl_fit_args* a, sdm_icl_cache* out) {
   c->B = B; c->H = H; c->D = kHeadDim;
   c->prec = prec;
   c->mode = a->scale_mode;
+  c->scoped = a->precision == SDM_ICL_PREC_SCOPED && prec == SDM_ICL_PREC_FP8_E4M3;
   c->n_max = n;
   c->n_alloc = round_up(n, kKeyTile);
   c->lengths.assign(a->lengths, a->lengths + B);
@@ -450,6 +482,8 @@ sdm_icl_status sdm_icl_attn_query_workspace_size(sdm_icl_cache c, int64_t n_quer
 sdm_icl_status sdm_icl_attn_query(sdm_icl_cache c, const void* q, const void* gate, int64_t R,
                                   void* out, void* ws, size_t ws_bytes, void* stream) {
   if (!live(c)) return fail(SDM_ICL_E_STATE, "query: unknown or released cache");
+  if (c->scoped && !scope_fp8())
+    return fail(SDM_ICL_E_STATE, "query: an FP8 cache built under the FP8 scope is used outside an enabled scope");
   if (R < 0) return fail(SDM_ICL_E_INVALID, "query: n_query < 0");
   if ((gate != nullptr) != (c->mode == SDM_ICL_SCALE_GATED_LOG))
     return fail(SDM_ICL_E_INVALID, c->mode == SDM_ICL_SCALE_GATED_LOG
@@ -534,6 +568,8 @@ sdm_icl_status sdm_icl_attn_cache_info(sdm_icl_cache c, sdm_icl_cache_info* info
 sdm_icl_status sdm_icl_attn_cache_export(sdm_icl_cache c, void* host_k, void* host_v,
                                          float* host_scales, void* stream) {
   if (!live(c)) return fail(SDM_ICL_E_STATE, "cache_export: unknown or released cache");
+  if (c->scoped && !scope_fp8())
+    return fail(SDM_ICL_E_STATE, "cache_export: an FP8 cache built under the FP8 scope is used outside an enabled scope");
   hipStream_t s = (hipStream_t)stream;
   const int64_t eb = c->prec == SDM_ICL_PREC_FP8_E4M3 ? 1 : 2;
   const int64_t BH = (int64_t)c->B * c->H, row_bytes = kHeadDim * eb;

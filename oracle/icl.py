@@ -45,7 +45,7 @@ import numpy as np
 from .numerics import E4M3_MAX, E4M3_VALUES, e4m3_encode, e4m3_round
 
 SCALE_NONE, SCALE_LOG, SCALE_GATED_LOG = 0, 1, 2
-PREC_FP16, PREC_FP8_E4M3, PREC_AUTO = 0, 1, 2
+PREC_FP16, PREC_FP8_E4M3, PREC_AUTO, PREC_SCOPED = 0, 1, 2, 3
 FP8_MIN_CONTEXT_ROWS = 8192
 
 
@@ -107,10 +107,19 @@ def scale_queries(q: np.ndarray, mode: int, k_h: Optional[np.ndarray],
 # Integrate FP8 attention and caching into TabICLv2", introduction)
 # ---------------------------------------------------------------------------
 
-def select_precision(n: int, requested: int) -> int:
-    """FP8 only above 8,192 unmasked context rows when precision is automatic."""
+def select_precision(n: int, requested: int, fp8_scope: bool = False) -> int:
+    """Precision of one attention call with n unmasked context rows.
+
+    AUTO: FP8 only above 8,192 unmasked context rows.  SCOPED: the rule of an
+    intermediate ICL layer under the opt-in FP8 scope of the TabICLv2 FP8
+    page (introduction): FP8 iff the scope enables it *and* n > 8,192, else
+    the normal precision; a final layer keeps normal precision by asking for
+    FP16.  Explicit FP16 / FP8 are honoured as given.
+    """
     if requested == PREC_AUTO:
         return PREC_FP8_E4M3 if n > FP8_MIN_CONTEXT_ROWS else PREC_FP16
+    if requested == PREC_SCOPED:
+        return PREC_FP8_E4M3 if (fp8_scope and n > FP8_MIN_CONTEXT_ROWS) else PREC_FP16
     return requested
 
 
@@ -271,7 +280,8 @@ def _lengths(n, B: int, N: int) -> np.ndarray:
 
 def fit(q: np.ndarray, k: np.ndarray, v: np.ndarray, n, scale_mode: int,
         precision: int, head_coef: Optional[np.ndarray] = None,
-        gate: Optional[np.ndarray] = None, keep_codes: bool = True) -> OracleCache:
+        gate: Optional[np.ndarray] = None, keep_codes: bool = True,
+        fp8_scope: bool = False) -> OracleCache:
     """Build the cache from context Q/K/V ``[B, N_pad, H, D]``.
 
     n: the valid rows, one int shared by all batch elements or one per
@@ -282,7 +292,7 @@ def fit(q: np.ndarray, k: np.ndarray, v: np.ndarray, n, scale_mode: int,
     """
     B, N, H, D = q.shape
     lengths = _lengths(n, B, N)
-    prec = select_precision(int(lengths.max()), precision)
+    prec = select_precision(int(lengths.max()), precision, fp8_scope)
     L32s = np.array([length_scalar(int(nb)) for nb in lengths], dtype=np.float32)
     k_hs = (np.stack([head_factors(L32s[b], head_coef) for b in range(B)])
             if scale_mode != SCALE_NONE else None)

@@ -156,3 +156,99 @@ def test_log_scale_validation():
     assert lib.sdm_icl_log_scale(0x1000, None, 1, 4, 8, 32, 10, coef, 1, None, 0x2000, None) == 2
     # zero rows is a no-op
     assert lib.sdm_icl_log_scale(None, None, 1, 0, 8, 64, 10, coef, 1, None, None, None) == 0
+
+
+# ----------------------------------------------------------------- FP8 scope (host logic)
+
+def test_scope_stack_nesting_inherit_and_errors():
+    lib = B.lib()
+    assert B.sdm_icl_scope_fp8() == 0                     # no scope: disabled
+    B.sdm_icl_scope_push(B.SDM_ICL_SCOPE_ENABLE)
+    try:
+        assert B.sdm_icl_scope_fp8() == 1
+        B.sdm_icl_scope_push(B.SDM_ICL_SCOPE_INHERIT)
+        assert B.sdm_icl_scope_fp8() == 1                 # inherits the enclosing ENABLE
+        B.sdm_icl_scope_push(B.SDM_ICL_SCOPE_DISABLE)
+        assert B.sdm_icl_scope_fp8() == 0
+        B.sdm_icl_scope_pop()
+        assert B.sdm_icl_scope_fp8() == 1                 # leaving restores the setting
+        B.sdm_icl_scope_pop()
+    finally:
+        B.sdm_icl_scope_pop()
+    assert B.sdm_icl_scope_fp8() == 0
+    assert lib.sdm_icl_scope_pop() == 6                   # nothing open
+    assert lib.sdm_icl_scope_push(7) == 1                 # unknown setting
+    for _ in range(256):
+        B.sdm_icl_scope_push(B.SDM_ICL_SCOPE_INHERIT)
+    assert lib.sdm_icl_scope_push(B.SDM_ICL_SCOPE_ENABLE) == 6   # depth limit
+    for _ in range(256):
+        B.sdm_icl_scope_pop()
+
+
+def test_scope_is_per_thread_in_the_library():
+    import threading
+    seen = []
+    B.sdm_icl_scope_push(B.SDM_ICL_SCOPE_ENABLE)
+    try:
+        t = threading.Thread(target=lambda: seen.append(B.sdm_icl_scope_fp8()))
+        t.start()
+        t.join()
+    finally:
+        B.sdm_icl_scope_pop()
+    assert seen == [0]
+
+
+def test_scoped_precision_matches_oracle():
+    for n in (1, 8192, 8193, 10 ** 6):
+        assert B.sdm_icl_select_precision(n, B.SDM_ICL_PREC_SCOPED) == \
+            icl.select_precision(n, icl.PREC_SCOPED, fp8_scope=False)
+        B.sdm_icl_scope_push(B.SDM_ICL_SCOPE_ENABLE)
+        try:
+            assert B.sdm_icl_select_precision(n, B.SDM_ICL_PREC_SCOPED) == \
+                icl.select_precision(n, icl.PREC_SCOPED, fp8_scope=True)
+            for req in (0, 1, 2):     # the scope leaves explicit and AUTO precision alone
+                assert B.sdm_icl_select_precision(n, req) == icl.select_precision(n, req)
+        finally:
+            B.sdm_icl_scope_pop()
+
+
+def test_optimize_is_context_local_and_restores_on_exceptions():
+    import asyncio
+    import threading
+    assert not B.fp8_scope_enabled()
+    with B.optimize(attention="fp8"):
+        assert B.fp8_scope_enabled()
+        with B.optimize(attention=None):
+            assert B.fp8_scope_enabled()
+        with pytest.raises(KeyError):
+            with B.optimize(attention="none"):
+                assert not B.fp8_scope_enabled()
+                raise KeyError("boom")
+        assert B.fp8_scope_enabled()
+        other = []
+        t = threading.Thread(target=lambda: other.append(B.fp8_scope_enabled()))
+        t.start()
+        t.join()
+        assert other == [False]                           # a new thread starts outside any scope
+    assert not B.fp8_scope_enabled()
+
+    async def task(enable, started, out):
+        if enable:
+            with B.optimize(attention="fp8"):
+                started.set()
+                await asyncio.sleep(0.01)
+                out.append(B.fp8_scope_enabled())
+        else:
+            await started.wait()
+            out.append(B.fp8_scope_enabled())
+
+    async def main():
+        started, a, b = asyncio.Event(), [], []
+        await asyncio.gather(task(True, started, a), task(False, started, b))
+        return a, b
+
+    a, b = asyncio.run(main())
+    assert a == [True] and b == [False]                   # tasks do not see each other's scope
+    with pytest.raises(ValueError):
+        with B.optimize(attention="int4"):
+            pass

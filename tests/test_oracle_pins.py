@@ -298,6 +298,22 @@ def test_auto_precision_follows_the_longest_context():
         icl.fit(z, z, z, [5, 5, 5], icl.SCALE_NONE, icl.PREC_FP16)
 
 
+def test_scoped_precision_is_the_intermediate_layer_rule():
+    """The TabICLv2 FP8 page: intermediate ICL layers use FP8 above 8,192
+    unmasked context rows, only inside the opt-in scope; outside it (and for
+    the final layer, which asks for FP16) attention keeps normal precision."""
+    S, F16, F8 = icl.PREC_SCOPED, icl.PREC_FP16, icl.PREC_FP8_E4M3
+    assert icl.select_precision(8193, S, fp8_scope=True) == F8
+    assert icl.select_precision(8192, S, fp8_scope=True) == F16
+    assert icl.select_precision(10 ** 6, S, fp8_scope=False) == F16
+    assert icl.select_precision(10 ** 6, F16, fp8_scope=True) == F16      # final layer
+    assert icl.select_precision(100, icl.PREC_AUTO, fp8_scope=False) == F16
+    assert icl.select_precision(8193, icl.PREC_AUTO, fp8_scope=False) == F8   # AUTO ignores the scope
+    z = np.zeros((1, 8200, 1, 64), dtype=np.float16)
+    assert icl.fit(z, z, z, 8200, icl.SCALE_NONE, S, fp8_scope=True).precision == F8
+    assert icl.fit(z, z, z, 8200, icl.SCALE_NONE, S).precision == F16
+
+
 def test_fp8_is_lossless_on_grid_inputs():
     """I10: when Q~, K, V already lie on the e4m3 grid with amax = 448 s, FP8
     quantisation changes nothing and the FP8 result equals the FP16 one.  Each
