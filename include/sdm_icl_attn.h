@@ -170,6 +170,32 @@ sdm_icl_status sdm_icl_attn_cache_lengths(sdm_icl_cache cache, int64_t* host_len
 sdm_icl_status sdm_icl_attn_cache_export(sdm_icl_cache cache, void* host_k, void* host_v,
                                          float* host_scales, void* stream);
 
+typedef struct {
+  int32_t batch;              /* B >= 1 */
+  int32_t heads;              /* H, 1..128 */
+  int32_t head_dim;           /* D, must be 64 */
+  const int64_t* lengths;     /* host [B]: n_b >= 1 */
+  int32_t scale_mode;         /* SDM_ICL_SCALE_* the cache was fitted with */
+  int32_t precision;          /* FP16 or FP8_E4M3 (a resolved precision) */
+  const float* head_coef;     /* host float32 [H] iff scale_mode != NONE */
+  const void* host_k;         /* host [B, H, n, D], n = max n_b, as cache_export writes it:
+                                 e4m3 codes (1 byte) or fp16; rows >= n_b are ignored */
+  const void* host_v;         /* host [B, H, n, D], same element type */
+  const float* host_scales;   /* host float32 [3, B, H]: s_q, s_k, s_v (all 1 for FP16) */
+  void* stream;               /* hipStream_t */
+} sdm_icl_import_args;
+
+/* Rebuild a cache from what cache_export wrote (persistence, migration to
+ * another device or process; the pages' FP8 caches are migrated and
+ * preserved through chunking, "[FP8 3/4] ...", walkthrough).  FP8 codes and
+ * scales are taken as they are; the inverse scales the query quantiser needs
+ * are recovered exactly from s = fp32(amax/448) (the amax is an fp16 value),
+ * so queries on the imported cache reproduce those on the exported one bit
+ * for bit.  Scales that are not of that form are SDM_ICL_E_INVALID, as are
+ * e4m3 NaN codes (0x7F, 0xFF).  Allocates the cache on args->stream and
+ * synchronises that stream before it returns. */
+sdm_icl_status sdm_icl_attn_cache_import(const sdm_icl_import_args* args, sdm_icl_cache* out);
+
 /* Free a cache.  The memory is returned stream-ordered on the stream the cache
  * was fitted on; work on other streams that uses the cache must be complete
  * (or ordered before that stream) first.  A second release of the same handle

@@ -53,6 +53,14 @@ class CacheInfo(ctypes.Structure):
                 ("length_scalar", ctypes.c_float), ("device_bytes", ctypes.c_uint64)]
 
 
+class ImportArgs(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("lengths", ctypes.POINTER(ctypes.c_int64)), ("scale_mode", ctypes.c_int32),
+                ("precision", ctypes.c_int32), ("head_coef", ctypes.POINTER(ctypes.c_float)),
+                ("host_k", ctypes.c_void_p), ("host_v", ctypes.c_void_p),
+                ("host_scales", ctypes.POINTER(ctypes.c_float)), ("stream", ctypes.c_void_p)]
+
+
 # name -> (restype, argtypes), exactly the declarations of include/sdm_icl_attn.h
 _SIGNATURES = {
     "sdm_icl_attn_fit": (ctypes.c_int32, [ctypes.POINTER(FitArgs), ctypes.POINTER(ctypes.c_void_p)]),
@@ -66,6 +74,7 @@ _SIGNATURES = {
                                                    ctypes.c_void_p, ctypes.c_void_p]),
     "sdm_icl_attn_cache_lengths": (ctypes.c_int32, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
                                                     ctypes.POINTER(ctypes.c_float)]),
+    "sdm_icl_attn_cache_import": (ctypes.c_int32, [ctypes.POINTER(ImportArgs), ctypes.POINTER(ctypes.c_void_p)]),
     "sdm_icl_attn_release": (ctypes.c_int32, [ctypes.c_void_p]),
     "sdm_icl_log_scale": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                            ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
@@ -356,6 +365,39 @@ def sdm_icl_attn_cache_lengths(cache: Cache):
     _check(lib().sdm_icl_attn_cache_lengths(cache.handle, n.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                                             L.ctypes.data_as(ctypes.POINTER(ctypes.c_float))))
     return n, L
+
+
+def import_args(k: np.ndarray, v: np.ndarray, scales: np.ndarray, lengths, scale_mode: int,
+                precision: int, head_coef=None, stream=None):
+    """(ImportArgs, keep-alive tuple) for host arrays as cache_export returns them."""
+    k = np.ascontiguousarray(k)
+    v = np.ascontiguousarray(v)
+    Bn, H, n, D = k.shape
+    sc = np.ascontiguousarray(scales, dtype=np.float32)
+    ls = [int(x) for x in np.asarray(lengths, dtype=np.int64).reshape(-1)]
+    if len(ls) == 1:
+        ls = ls * Bn
+    la = (ctypes.c_int64 * Bn)(*ls)
+    coef = None
+    coef_np = None
+    if head_coef is not None:
+        coef_np = np.ascontiguousarray(head_coef, dtype=np.float32)
+        coef = coef_np.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    args = ImportArgs(batch=Bn, heads=H, head_dim=D, lengths=la, scale_mode=scale_mode,
+                      precision=precision, head_coef=coef, host_k=k.ctypes.data, host_v=v.ctypes.data,
+                      host_scales=sc.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                      stream=stream)
+    return args, (k, v, sc, la, coef_np)
+
+
+def sdm_icl_attn_cache_import(k: np.ndarray, v: np.ndarray, scales: np.ndarray, lengths,
+                              scale_mode: int, precision: int, head_coef=None, stream=None) -> Cache:
+    """Rebuild a cache from ``cache_export``'s arrays (K, V ``[B, H, n, 64]``,
+    scales ``[3, B, H]``)."""
+    args, keep = import_args(k, v, scales, lengths, scale_mode, precision, head_coef, _stream_ptr(stream))
+    handle = ctypes.c_void_p()
+    _check(lib().sdm_icl_attn_cache_import(ctypes.byref(args), ctypes.byref(handle)))
+    return Cache(handle.value)
 
 
 def sdm_icl_attn_release(cache: Cache) -> None:

@@ -259,6 +259,103 @@ AttnArgs attn_args(const sdm_icl_cache_s* c) {
   return a;
 }
 
+// A cache object with its lengths, length scalars, head factors and split
+// plan, and its one device allocation ([kc][vt][scales 3BH][inv 3BH][n_b B]
+// [k_h BH]) with n_b and k_h uploaded; K/V, scales and inverse scales are
+// left for the caller to fill.
+sdm_icl_status new_cache(int B, int H, const int64_t* lengths, int mode, int prec, const float* coef,
+                         int dev, int cus, hipStream_t s, const char* who, sdm_icl_cache_s** out) {
+  int64_t n = 0;
+  for (int b = 0; b < B; ++b) n = lengths[b] > n ? lengths[b] : n;
+  const int64_t eb = prec == SDM_ICL_PREC_FP8_E4M3 ? 1 : 2;
+  auto* c = new sdm_icl_cache_s();
+  c->magic = kMagic;
+  c->device = dev;
+  c->stream = s;
+  c->B = B; c->H = H; c->D = kHeadDim;
+  c->prec = prec;
+  c->mode = mode;
+  c->scoped = false;
+  c->n_max = n;
+  c->n_alloc = round_up(n, kKeyTile);
+  c->lengths.assign(lengths, lengths + B);
+  c->L32.resize(B);
+  c->kh.assign((size_t)B * H, 0);
+  for (int b = 0; b < B; ++b) {
+    c->L32[b] = length_scalar(c->lengths[b]);
+    if (mode != SDM_ICL_SCALE_NONE) {
+      HeadFactors f;
+      head_factors(c->lengths[b], coef, H, &f);
+      std::memcpy(&c->kh[(size_t)b * H], f.bits, sizeof(uint16_t) * H);
+    }
+  }
+  plan_splits(n, cus, (int64_t)B * H, &c->splits, &c->tiles_per_split);
+
+  const size_t kv_bytes = (size_t)B * H * c->n_alloc * kHeadDim * eb;
+  const size_t sc_bytes = (size_t)6 * B * H * sizeof(float);
+  const size_t len_bytes = (size_t)B * sizeof(int64_t);
+  const size_t kh_bytes = (size_t)B * H * sizeof(uint16_t);
+  c->bytes = 2 * kv_bytes + sc_bytes + len_bytes + kh_bytes;
+  hipError_t e = hipMallocAsync(&c->block, c->bytes, s);
+  if (e != hipSuccess) {
+    delete c;
+    return hip_fail(e, (std::string(who) + ": cache allocation").c_str());
+  }
+  c->kc = c->block;
+  c->vt = (char*)c->block + kv_bytes;
+  c->scales = (float*)((char*)c->block + 2 * kv_bytes);
+  c->inv = c->scales + 3 * B * H;
+  c->n_dev = (int64_t*)((char*)c->block + 2 * kv_bytes + sc_bytes);  // 8-byte aligned: 24BH bytes of scales
+  c->kh_dev = (uint16_t*)((char*)c->n_dev + len_bytes);
+  // the host copies live as long as the cache, so the source outlives the copy
+  e = hipMemcpyAsync(c->n_dev, c->lengths.data(), len_bytes, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(c->kh_dev, c->kh.data(), kh_bytes, hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) {
+    (void)hipFreeAsync(c->block, s);
+    delete c;
+    return hip_fail(e, (std::string(who) + ": length upload").c_str());
+  }
+  *out = c;
+  return SDM_ICL_OK;
+}
+
+void register_cache(sdm_icl_cache_s* c) {
+  std::lock_guard<std::mutex> lk(g_registry_mu);
+  g_registry.insert(c);
+}
+
+float f16_bits_to_f32(uint16_t h) {
+  const uint32_t sign = (uint32_t)(h >> 15) << 31;
+  const int exp = (h >> 10) & 31;
+  const uint32_t man = h & 1023;
+  float v;
+  if (exp == 0) v = std::ldexp((float)man, -24);                      // subnormal or zero
+  else if (exp == 31) v = man ? NAN : INFINITY;
+  else v = std::ldexp((float)(man | 1024), exp - 25);
+  uint32_t bits;
+  std::memcpy(&bits, &v, 4);
+  bits |= sign;
+  std::memcpy(&v, &bits, 4);
+  return v;
+}
+
+// The inverse scale fit derived together with s = fp32(a / 448), where a is
+// the fp16 amax: a is the one fp16 value whose quotient by 448 rounds to s
+// (distinct fp16 values differ by at least 2^-11 relative, so their fp32
+// quotients differ).  s = 1 stands for a = 0 or a = 448, both giving inv = 1.
+bool inverse_from_scale(float s, float* inv) {
+  if (!(s > 0.f) || !std::isfinite(s)) return false;
+  if (s == 1.f) { *inv = 1.f; return true; }
+  const uint16_t h0 = f32_to_f16_bits(s * 448.0f);
+  for (int d = -1; d <= 1; ++d) {
+    const uint16_t h = (uint16_t)(h0 + d);
+    const float a = f16_bits_to_f32(h);
+    if (!(a > 0.f) || !std::isfinite(a)) continue;
+    if (a / 448.0f == s) { *inv = 448.0f / a; return true; }
+  }
+  return false;
+}
+
 }  // namespace
 
 extern "C" {
@@ -356,50 +453,11 @@ sdm_icl_status sdm_icl_attn_fit(const sdm_icl_fit_args* a, sdm_icl_cache* out) {
   const int B = a->batch, H = a->heads;
   const int prec = resolve_precision(n, a->precision);
   const int64_t eb = prec == SDM_ICL_PREC_FP8_E4M3 ? 1 : 2;
-  auto* c = new sdm_icl_cache_s();
-  c->magic = kMagic;
-  c->device = dev;
-  c->stream = s;
-  c->B = B; c->H = H; c->D = kHeadDim;
-  c->prec = prec;
-  c->mode = a->scale_mode;
+  sdm_icl_cache_s* c = nullptr;
+  if ((st = new_cache(B, H, a->lengths, a->scale_mode, prec, a->head_coef, dev, di.cus, s, "fit", &c)))
+    return st;
   c->scoped = a->precision == SDM_ICL_PREC_SCOPED && prec == SDM_ICL_PREC_FP8_E4M3;
-  c->n_max = n;
-  c->n_alloc = round_up(n, kKeyTile);
-  c->lengths.assign(a->lengths, a->lengths + B);
-  c->L32.resize(B);
-  c->kh.assign((size_t)B * H, 0);
-  for (int b = 0; b < B; ++b) {
-    c->L32[b] = length_scalar(c->lengths[b]);
-    if (a->scale_mode != SDM_ICL_SCALE_NONE) {
-      HeadFactors f;
-      head_factors(c->lengths[b], a->head_coef, H, &f);
-      std::memcpy(&c->kh[(size_t)b * H], f.bits, sizeof(uint16_t) * H);
-    }
-  }
-  plan_splits(n, di.cus, (int64_t)B * H, &c->splits, &c->tiles_per_split);
-
-  const size_t kv_bytes = (size_t)B * H * c->n_alloc * kHeadDim * eb;
-  const size_t sc_bytes = (size_t)6 * B * H * sizeof(float);
-  const size_t len_bytes = (size_t)B * sizeof(int64_t);
-  const size_t kh_bytes = (size_t)B * H * sizeof(uint16_t);
-  c->bytes = 2 * kv_bytes + sc_bytes + len_bytes + kh_bytes;
-  hipError_t e = hipMallocAsync(&c->block, c->bytes, s);
-  if (e != hipSuccess) { delete c; return hip_fail(e, "fit: cache allocation"); }
-  c->kc = c->block;
-  c->vt = (char*)c->block + kv_bytes;
-  c->scales = (float*)((char*)c->block + 2 * kv_bytes);
-  c->inv = c->scales + 3 * B * H;
-  c->n_dev = (int64_t*)((char*)c->block + 2 * kv_bytes + sc_bytes);  // 8-byte aligned: 24BH bytes of scales
-  c->kh_dev = (uint16_t*)((char*)c->n_dev + len_bytes);
-  // the host copies live as long as the cache, so the source outlives the copy
-  e = hipMemcpyAsync(c->n_dev, c->lengths.data(), len_bytes, hipMemcpyHostToDevice, s);
-  if (e == hipSuccess) e = hipMemcpyAsync(c->kh_dev, c->kh.data(), kh_bytes, hipMemcpyHostToDevice, s);
-  if (e != hipSuccess) {
-    (void)hipFreeAsync(c->block, s);
-    delete c;
-    return hip_fail(e, "fit: length upload");
-  }
+  hipError_t e = hipSuccess;
   const Factors fac{c->kh_dev, HeadFactors{}};
 
   // temporaries: amax scratch and the context Q operand
@@ -463,10 +521,7 @@ sdm_icl_status sdm_icl_attn_fit(const sdm_icl_fit_args* a, sdm_icl_cache* out) {
     delete c;
     return hip_fail(e, "fit: launch");
   }
-  {
-    std::lock_guard<std::mutex> lk(g_registry_mu);
-    g_registry.insert(c);
-  }
+  register_cache(c);
   *out = c;
   return SDM_ICL_OK;
 }
@@ -614,6 +669,86 @@ sdm_icl_status sdm_icl_attn_cache_lengths(sdm_icl_cache c, int64_t* host_lengths
   if (!live(c)) return fail(SDM_ICL_E_STATE, "cache_lengths: unknown or released cache");
   if (host_lengths) std::memcpy(host_lengths, c->lengths.data(), sizeof(int64_t) * c->B);
   if (host_length_scalars) std::memcpy(host_length_scalars, c->L32.data(), sizeof(float) * c->B);
+  return SDM_ICL_OK;
+}
+
+sdm_icl_status sdm_icl_attn_cache_import(const sdm_icl_import_args* a, sdm_icl_cache* out) {
+  if (!a || !out) return fail(SDM_ICL_E_INVALID, "import: null args or out");
+  if (a->batch < 1 || a->heads < 1) return fail(SDM_ICL_E_INVALID, "import: batch and heads must be >= 1");
+  if (a->heads > kMaxHeads) return fail(SDM_ICL_E_UNSUPPORTED, "import: at most %d heads", kMaxHeads);
+  if (a->head_dim != kHeadDim) return fail(SDM_ICL_E_UNSUPPORTED, "import: head_dim must be 64 (got %d)", a->head_dim);
+  if (!a->lengths || !a->host_k || !a->host_v || !a->host_scales)
+    return fail(SDM_ICL_E_INVALID, "import: lengths, host_k, host_v and host_scales are required");
+  if (a->scale_mode < SDM_ICL_SCALE_NONE || a->scale_mode > SDM_ICL_SCALE_GATED_LOG)
+    return fail(SDM_ICL_E_INVALID, "import: unknown scale_mode %d", a->scale_mode);
+  if ((a->head_coef != nullptr) != (a->scale_mode != SDM_ICL_SCALE_NONE))
+    return fail(SDM_ICL_E_INVALID, "import: head_coef must be given exactly when scale_mode is LOG or GATED_LOG");
+  if (a->precision != SDM_ICL_PREC_FP16 && a->precision != SDM_ICL_PREC_FP8_E4M3)
+    return fail(SDM_ICL_E_INVALID, "import: precision must be FP16 or FP8_E4M3 (got %d)", a->precision);
+  const int B = a->batch, H = a->heads;
+  int64_t n = 0;
+  for (int b = 0; b < B; ++b) {
+    if (a->lengths[b] < 1 || a->lengths[b] > ((int64_t)1 << 31))
+      return fail(SDM_ICL_E_INVALID, "import: lengths[%d] = %lld out of range", b, (long long)a->lengths[b]);
+    n = a->lengths[b] > n ? a->lengths[b] : n;
+  }
+  const bool fp8 = a->precision == SDM_ICL_PREC_FP8_E4M3;
+  const int64_t eb = fp8 ? 1 : 2, BH = (int64_t)B * H;
+  // scales and the inverse scales they imply
+  std::vector<float> sc(6 * BH);
+  for (int64_t i = 0; i < 3 * BH; ++i) {
+    const float sv = a->host_scales[i];
+    float inv;
+    if (!fp8) {
+      if (sv != 1.f) return fail(SDM_ICL_E_INVALID, "import: FP16 caches have unit scales");
+      inv = 1.f;
+    } else if (!inverse_from_scale(sv, &inv)) {
+      return fail(SDM_ICL_E_INVALID, "import: scale %lld (%g) is not fp32(amax/448) of an fp16 amax", (long long)i, (double)sv);
+    }
+    sc[i] = sv;
+    sc[3 * BH + i] = inv;
+  }
+  // host images of the device layout: K [bh][n_alloc][64], V [bh][tiles][64 d][64 keys]
+  const int64_t n_alloc = round_up(n, kKeyTile), tiles = n_alloc / kKeyTile;
+  const size_t kv_bytes = (size_t)BH * n_alloc * kHeadDim * eb;
+  std::vector<unsigned char> hk(kv_bytes, 0), hv(kv_bytes, 0);
+  const unsigned char* sk = (const unsigned char*)a->host_k;
+  const unsigned char* sv = (const unsigned char*)a->host_v;
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < H; ++h) {
+      const int64_t bh = (int64_t)b * H + h, nb = a->lengths[b];
+      const unsigned char* kr = sk + (size_t)bh * n * kHeadDim * eb;
+      const unsigned char* vr = sv + (size_t)bh * n * kHeadDim * eb;
+      if (fp8)
+        for (int64_t i = 0; i < nb * kHeadDim; ++i)
+          if ((kr[i] & 0x7F) == 0x7F || (vr[i] & 0x7F) == 0x7F)
+            return fail(SDM_ICL_E_INVALID, "import: NaN e4m3 code in batch %d head %d", b, h);
+      std::memcpy(hk.data() + (size_t)bh * n_alloc * kHeadDim * eb, kr, (size_t)(nb * kHeadDim * eb));
+      for (int64_t key = 0; key < nb; ++key)
+        for (int d = 0; d < kHeadDim; ++d)
+          std::memcpy(hv.data() + ((((size_t)bh * tiles + key / kKeyTile) * kHeadDim + d) * kKeyTile + key % kKeyTile) * eb,
+                      vr + ((size_t)key * kHeadDim + d) * eb, (size_t)eb);
+    }
+
+  int dev;
+  DeviceInfo di;
+  sdm_icl_status st = current_device(&dev, &di);
+  if (st) return st;
+  hipStream_t s = (hipStream_t)a->stream;
+  sdm_icl_cache_s* c = nullptr;
+  if ((st = new_cache(B, H, a->lengths, a->scale_mode, a->precision, a->head_coef, dev, di.cus, s, "import", &c)))
+    return st;
+  hipError_t e = hipMemcpyAsync(c->kc, hk.data(), kv_bytes, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(c->vt, hv.data(), kv_bytes, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(c->scales, sc.data(), sc.size() * sizeof(float), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);  // the host images go out of scope below
+  if (e != hipSuccess) {
+    (void)hipFreeAsync(c->block, s);
+    delete c;
+    return hip_fail(e, "import: upload");
+  }
+  register_cache(c);
+  *out = c;
   return SDM_ICL_OK;
 }
 

@@ -252,3 +252,54 @@ def test_optimize_is_context_local_and_restores_on_exceptions():
     with pytest.raises(ValueError):
         with B.optimize(attention="int4"):
             pass
+
+
+# ----------------------------------------------------------------- cache import (host validation)
+
+def _import_status(k, v, sc, lengths=(3,), mode=0, prec=1, coef=None):
+    args, keep = B.import_args(k, v, sc, list(lengths), mode, prec, coef)
+    h = ctypes.c_void_p()
+    st = B.lib().sdm_icl_attn_cache_import(ctypes.byref(args), ctypes.byref(h))
+    return st
+
+
+def test_import_validates_before_touching_the_device():
+    k = np.zeros((1, 2, 3, 64), dtype=np.uint8)
+    sc = np.ones((3, 1, 2), dtype=np.float32)
+    passed = lambda st: st not in (1, 2)      # got past host validation (no GPU here)
+    assert passed(_import_status(k, k, sc))
+    assert _import_status(k, k, sc, prec=2) == 1                     # AUTO is not a resolved precision
+    assert _import_status(k, k, sc, mode=1) == 1                     # LOG without coefficients
+    bad = k.copy(); bad[0, 1, 2, 5] = 0xFF                           # NaN code
+    assert _import_status(bad, k, sc) == 1
+    assert _import_status(k, bad, sc) == 1
+    bad[0, 1, 2, 5] = 0x7E                                           # 448: fine
+    assert passed(_import_status(bad, k, sc))
+    sc2 = sc.copy(); sc2[1, 0, 1] = 0.3                              # not amax/448 of an fp16 amax
+    assert _import_status(k, k, sc2) == 1
+    assert "scale" in B.sdm_icl_last_error()
+    sc2[1, 0, 1] = -1.0
+    assert _import_status(k, k, sc2) == 1
+    k16 = np.zeros((1, 2, 3, 64), dtype=np.float16)
+    assert passed(_import_status(k16, k16, sc, prec=0))
+    sc3 = sc.copy(); sc3[2, 0, 0] = 0.5                              # FP16 caches have unit scales
+    assert _import_status(k16, k16, sc3, prec=0) == 1
+
+
+def test_import_accepts_the_scale_of_every_fp16_amax():
+    """fit writes s = fp32(a/448) for an fp16 amax a; import must recognise
+    every such s (it recovers a, and with it the exact inverse scale)."""
+    k = np.zeros((1, 1, 1, 64), dtype=np.uint8)
+    a = _all_finite_fp16_positive()
+    bad = []
+    for i in range(a.size):
+        s = icl.fp8_scale(a[i])[0]
+        sc = np.full((3, 1, 1), s, dtype=np.float32)
+        if _import_status(k, k, sc, lengths=(1,)) == 1:
+            bad.append(float(a[i]))
+    assert not bad, bad[:5]
+
+
+def _all_finite_fp16_positive():
+    v = np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16)
+    return v[v > 0]
