@@ -126,6 +126,8 @@ typedef struct {
   int64_t keys_per_split;  /* rows of each KV split (multiple of 64) */
   float length_scalar;     /* L32 (per-batch lengths: that of batch element 0) */
   uint64_t device_bytes;   /* bytes of device memory the cache holds */
+  int32_t offloaded;       /* 1 while K/V live in pinned host memory (cache_offload) */
+  int32_t stream_chunk_splits; /* splits per streamed chunk while offloaded, else 0 */
 } sdm_icl_cache_info;
 
 /* Build the K/V cache from the context (model.fit) and, if out_ctx != NULL,
@@ -195,6 +197,22 @@ typedef struct {
  * e4m3 NaN codes (0x7F, 0xFF).  Allocates the cache on args->stream and
  * synchronises that stream before it returns. */
 sdm_icl_status sdm_icl_attn_cache_import(const sdm_icl_import_args* args, sdm_icl_cache* out);
+
+/* Host offload ("[FP8 3/4] ...", introduction: cache chunking and CPU
+ * offloading are supported).  cache_offload moves the cache's K/V into pinned
+ * host memory and keeps only scales, lengths and factors on the device;
+ * cache_restore moves them back.  Both synchronise `stream` and are no-ops
+ * when the cache is already in that state; no query may be in flight on the
+ * cache meanwhile.  Queries on an offloaded cache stream K/V from host memory
+ * in chunks of whole KV splits through two staging buffers in the caller's
+ * workspace (query_workspace_size grows by 2 x 2 chunk buffers of K and V);
+ * chunk_bytes bounds one chunk's K bytes (0: 64 MiB; at least one split),
+ * copying on a stream the cache owns while the split kernel runs on
+ * the caller's stream, then combine as usual: the results are bit-identical
+ * to those of the resident cache.  Queries on one offloaded cache must not
+ * overlap (the cache's copy stream and events are shared). */
+sdm_icl_status sdm_icl_attn_cache_offload(sdm_icl_cache cache, size_t chunk_bytes, void* stream);
+sdm_icl_status sdm_icl_attn_cache_restore(sdm_icl_cache cache, void* stream);
 
 /* Free a cache.  The memory is returned stream-ordered on the stream the cache
  * was fitted on; work on other streams that uses the cache must be complete

@@ -50,7 +50,8 @@ class CacheInfo(ctypes.Structure):
                 ("precision", ctypes.c_int32), ("scale_mode", ctypes.c_int32),
                 ("kv_splits", ctypes.c_int32), ("n_valid", ctypes.c_int64),
                 ("rows_alloc", ctypes.c_int64), ("keys_per_split", ctypes.c_int64),
-                ("length_scalar", ctypes.c_float), ("device_bytes", ctypes.c_uint64)]
+                ("length_scalar", ctypes.c_float), ("device_bytes", ctypes.c_uint64),
+                ("offloaded", ctypes.c_int32), ("stream_chunk_splits", ctypes.c_int32)]
 
 
 class ImportArgs(ctypes.Structure):
@@ -75,6 +76,8 @@ _SIGNATURES = {
     "sdm_icl_attn_cache_lengths": (ctypes.c_int32, [ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64),
                                                     ctypes.POINTER(ctypes.c_float)]),
     "sdm_icl_attn_cache_import": (ctypes.c_int32, [ctypes.POINTER(ImportArgs), ctypes.POINTER(ctypes.c_void_p)]),
+    "sdm_icl_attn_cache_offload": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "sdm_icl_attn_cache_restore": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p]),
     "sdm_icl_attn_release": (ctypes.c_int32, [ctypes.c_void_p]),
     "sdm_icl_log_scale": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                            ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
@@ -398,6 +401,17 @@ def sdm_icl_attn_cache_import(k: np.ndarray, v: np.ndarray, scales: np.ndarray, 
     handle = ctypes.c_void_p()
     _check(lib().sdm_icl_attn_cache_import(ctypes.byref(args), ctypes.byref(handle)))
     return Cache(handle.value)
+
+
+def sdm_icl_attn_cache_offload(cache: Cache, chunk_bytes: int = 0, stream=None) -> None:
+    """Move the cache's K/V to pinned host memory; queries then stream it in
+    chunks of at most ``chunk_bytes`` of K (0: the library's default)."""
+    _check(lib().sdm_icl_attn_cache_offload(cache.handle, int(chunk_bytes), _stream_ptr(stream)))
+
+
+def sdm_icl_attn_cache_restore(cache: Cache, stream=None) -> None:
+    """Move an offloaded cache's K/V back into device memory."""
+    _check(lib().sdm_icl_attn_cache_restore(cache.handle, _stream_ptr(stream)))
 
 
 def sdm_icl_attn_release(cache: Cache) -> None:

@@ -281,7 +281,7 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
   const int bh = blockIdx.z;
   const int b = bh / a.heads, h = bh - b * a.heads;
   const int64_t q0 = (int64_t)blockIdx.x * QT;
-  const int split = blockIdx.y;
+  const int split = (int)blockIdx.y + a.split_base;
   const int64_t n = a.n_b[b];                          // keys of this batch element
   const int64_t q_valid = a.ctx ? n : a.q_rows_valid;  // its valid query rows
 
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
   auto load_stage = [&](int64_t t, Stage<EB, R>& st) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      const int64_t off = t * 64 * 64 * EB + (int64_t)(tid + i * NT) * 16 * EB;
+      const int64_t off = (t - a.tile_base) * 64 * 64 * EB + (int64_t)(tid + i * NT) * 16 * EB;
       const i32x4* kp = reinterpret_cast<const i32x4*>(kg + off);
       const i32x4* vp = reinterpret_cast<const i32x4*>(vg + off);
 #pragma unroll
@@ -552,7 +552,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 }  // namespace
 
-hipError_t launch_attention(const AttnArgs& a, int prec, bool split, hipStream_t s) {
+hipError_t launch_attention(const AttnArgs& a, int prec, bool split, hipStream_t s, int grid_splits) {
   // FP8 takes two 32-row query groups per wavefront (more MFMA work per LDS
   // read and per softmax step); split-KV calls with at most 128 rows use
   // two-wavefront workgroups so that one small query batch still fills the
@@ -560,7 +560,8 @@ hipError_t launch_attention(const AttnArgs& a, int prec, bool split, hipStream_t
   // large).
   const int64_t rows = split ? a.q_rows_valid : a.out_rows;
   auto go = [&](auto kern, int qt, int waves) {
-    const dim3 grid((unsigned)((rows + qt - 1) / qt), (unsigned)a.splits, (unsigned)a.bh_count);
+    const dim3 grid((unsigned)((rows + qt - 1) / qt), (unsigned)(grid_splits > 0 ? grid_splits : a.splits),
+                    (unsigned)a.bh_count);
     hipLaunchKernelGGL(kern, grid, dim3(waves * 64), 0, s, a);
   };
   if (prec == kPrecFp8) {

@@ -39,7 +39,11 @@ struct AttnArgs {
   int32_t ctx;            // 1: the query rows are the context rows, so batch element b
                           // has n_b valid query rows (q_rows_valid is then their maximum)
   int32_t tiles_per_split;
-  int32_t splits;
+  int32_t splits;         // total splits of the plan (partials are [.][.][splits][.])
+  int32_t split_base;     // plan index of the launch's first split (blockIdx.y = 0)
+  int64_t tile_base;      // plan index of the first key tile held at kc / vt (n_alloc rows per
+                          // (b,h) from there on): 0 for a resident cache, a chunk's first
+                          // tile when the cache is streamed from host memory
   int32_t heads;
   int32_t bh_count;       // B*H
   float tau_log2e;        // log2(e) / sqrt(D)
@@ -81,8 +85,10 @@ hipError_t launch_pack_kv(const uint16_t* k, const uint16_t* v, int B, int64_t r
                           const float* inv_v, void* kc, void* vt, hipStream_t s);
 
 // K3 / K4: flash attention over the cache.  split == false writes normalised
-// fp16 rows to a.out; split == true writes per-split partials.
-hipError_t launch_attention(const AttnArgs& a, int prec, bool split, hipStream_t s);
+// fp16 rows to a.out; split == true writes per-split partials.  The grid
+// covers grid_splits splits from a.split_base on (0: all a.splits).
+hipError_t launch_attention(const AttnArgs& a, int prec, bool split, hipStream_t s,
+                            int grid_splits = 0);
 
 // K5: merge the splits of every (b, h, row) in a fixed order and write fp16 rows.
 hipError_t launch_combine(const float* part_o, const float* part_ml, const float* s_v,

@@ -8,6 +8,7 @@
 // except cache_export.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -40,6 +41,14 @@ struct sdm_icl_cache_s {
   int64_t* n_dev;
   uint16_t* kh_dev;
   size_t bytes;
+  // host offload: K/V in pinned host memory, streamed through the query
+  // workspace in chunks of chunk_splits splits
+  size_t kv_bytes;                // bytes of K (and of V)
+  bool offloaded;
+  unsigned char* host_kv;         // [kc][vt] when offloaded
+  int32_t chunk_splits;
+  hipStream_t copy_stream;
+  hipEvent_t ev_start, ev_ready[2], ev_free[2];
 };
 
 namespace {
@@ -223,9 +232,15 @@ struct TimedLaunch {
 };
 
 struct QueryLayout {
-  size_t q_off, po_off, ml_off, total;
+  size_t q_off, po_off, ml_off, stage_off = 0, stage_bytes = 0, total;
   int64_t q_rows_alloc;
 };
+
+// Bytes of one streamed chunk of K (or of V): chunk_splits splits of every (b, h).
+size_t chunk_bytes(const sdm_icl_cache_s* c) {
+  const int64_t eb = c->prec == SDM_ICL_PREC_FP8_E4M3 ? 1 : 2;
+  return (size_t)c->B * c->H * c->chunk_splits * c->tiles_per_split * kKeyTile * kHeadDim * eb;
+}
 
 QueryLayout query_layout(const sdm_icl_cache_s* c, int64_t R) {
   QueryLayout L;
@@ -240,6 +255,11 @@ QueryLayout query_layout(const sdm_icl_cache_s* c, int64_t R) {
     off += (size_t)round_up((int64_t)c->B * c->H * R * c->splits * 2 * 4, 256);
   } else {
     L.ml_off = off;
+  }
+  if (c->offloaded) {  // two staging buffers of one chunk's K and V
+    L.stage_off = off;
+    L.stage_bytes = chunk_bytes(c);
+    off += 2 * 2 * L.stage_bytes;
   }
   L.total = off;
   return L;
@@ -296,6 +316,12 @@ sdm_icl_status new_cache(int B, int H, const int64_t* lengths, int mode, int pre
   const size_t len_bytes = (size_t)B * sizeof(int64_t);
   const size_t kh_bytes = (size_t)B * H * sizeof(uint16_t);
   c->bytes = 2 * kv_bytes + sc_bytes + len_bytes + kh_bytes;
+  c->kv_bytes = kv_bytes;
+  c->offloaded = false;
+  c->host_kv = nullptr;
+  c->chunk_splits = 0;
+  c->copy_stream = nullptr;
+  c->ev_start = c->ev_ready[0] = c->ev_ready[1] = c->ev_free[0] = c->ev_free[1] = nullptr;
   hipError_t e = hipMallocAsync(&c->block, c->bytes, s);
   if (e != hipSuccess) {
     delete c;
@@ -317,6 +343,43 @@ sdm_icl_status new_cache(int B, int H, const int64_t* lengths, int mode, int pre
   }
   *out = c;
   return SDM_ICL_OK;
+}
+
+// Point scales / inv / n_b / k_h into a metadata region laid out as
+// [scales 3BH][inv 3BH][n_b B][k_h BH] (for an offloaded cache that region is
+// the whole device block).
+void set_meta(sdm_icl_cache_s* c, void* meta) {
+  const int64_t BH = (int64_t)c->B * c->H;
+  c->scales = (float*)meta;
+  c->inv = c->scales + 3 * BH;
+  c->n_dev = (int64_t*)((char*)meta + 6 * BH * sizeof(float));
+  c->kh_dev = (uint16_t*)((char*)c->n_dev + c->B * sizeof(int64_t));
+}
+
+// Streaming state of an offloaded cache: chunks of about 64 MiB of K (and as
+// much V), a copy stream at the default priority and the events that order
+// it with the caller's stream.
+constexpr size_t kChunkTarget = (size_t)64 << 20;
+
+hipError_t create_streaming(sdm_icl_cache_s* c, size_t chunk_target) {
+  const int64_t eb = c->prec == SDM_ICL_PREC_FP8_E4M3 ? 1 : 2;
+  const size_t per_split = (size_t)c->B * c->H * c->tiles_per_split * kKeyTile * kHeadDim * eb;
+  int64_t cs = (int64_t)((chunk_target ? chunk_target : kChunkTarget) / per_split);
+  c->chunk_splits = (int32_t)std::max<int64_t>(1, std::min<int64_t>(cs, c->splits));
+  hipError_t e = hipStreamCreateWithFlags(&c->copy_stream, hipStreamNonBlocking);
+  hipEvent_t* evs[] = {&c->ev_start, &c->ev_ready[0], &c->ev_ready[1], &c->ev_free[0], &c->ev_free[1]};
+  for (hipEvent_t* ev : evs)
+    if (e == hipSuccess) e = hipEventCreateWithFlags(ev, hipEventDisableTiming);
+  return e;
+}
+
+void destroy_streaming(sdm_icl_cache_s* c) {
+  hipEvent_t evs[] = {c->ev_start, c->ev_ready[0], c->ev_ready[1], c->ev_free[0], c->ev_free[1]};
+  for (hipEvent_t ev : evs)
+    if (ev) (void)hipEventDestroy(ev);
+  if (c->copy_stream) (void)hipStreamDestroy(c->copy_stream);
+  c->copy_stream = nullptr;
+  c->ev_start = c->ev_ready[0] = c->ev_ready[1] = c->ev_free[0] = c->ev_free[1] = nullptr;
 }
 
 void register_cache(sdm_icl_cache_s* c) {
@@ -354,6 +417,73 @@ bool inverse_from_scale(float s, float* inv) {
     if (a / 448.0f == s) { *inv = 448.0f / a; return true; }
   }
   return false;
+}
+
+
+// Attention of one query call over an offloaded cache: the plan's splits are
+// taken chunk_splits at a time; chunk i's K and V tiles of every (b, h) are
+// copied from pinned host memory into staging buffer i % 2 on the cache's
+// copy stream while the compute stream runs the split kernel on chunk i - 1.
+// Events order the two streams: a chunk is computed only after its copy
+// landed, and a buffer is refilled only after the kernel that read it.
+hipError_t streamed_attention(sdm_icl_cache_s* c, AttnArgs at, char* w, const QueryLayout& L,
+                              uint16_t* out, hipStream_t s) {
+  const int64_t eb = c->prec == SDM_ICL_PREC_FP8_E4M3 ? 1 : 2;
+  const int64_t BH = (int64_t)c->B * c->H;
+  const int64_t tiles_total = c->n_alloc / kKeyTile;
+  const int64_t chunk_tiles = (int64_t)c->chunk_splits * c->tiles_per_split;
+  const size_t src_pitch = (size_t)c->n_alloc * kHeadDim * eb;       // one (b, h) of the cache
+  const size_t dst_pitch = (size_t)chunk_tiles * kKeyTile * kHeadDim * eb;
+  unsigned char* stage[2][2];  // [buffer][K, V]
+  for (int b = 0; b < 2; ++b)
+    for (int kv = 0; kv < 2; ++kv) stage[b][kv] = (unsigned char*)w + L.stage_off + (2 * b + kv) * L.stage_bytes;
+  const bool split = c->splits > 1;
+  if (split) {
+    at.part_o = (float*)(w + L.po_off);
+    at.part_ml = (float*)(w + L.ml_off);
+  } else {
+    at.out = out;
+  }
+  at.n_alloc = chunk_tiles * kKeyTile;
+  hipError_t e = hipEventRecord(c->ev_start, s);   // the workspace is free once s gets here
+  if (e == hipSuccess) e = hipStreamWaitEvent(c->copy_stream, c->ev_start, 0);
+  const int chunks = (c->splits + c->chunk_splits - 1) / c->chunk_splits;
+  for (int i = 0; i < chunks && e == hipSuccess; ++i) {
+    const int buf = i & 1;
+    const int64_t t0 = (int64_t)i * chunk_tiles;
+    const int64_t nt = std::min(chunk_tiles, tiles_total - t0);
+    if (i >= 2) e = hipStreamWaitEvent(c->copy_stream, c->ev_free[buf], 0);
+    for (int kv = 0; kv < 2 && e == hipSuccess; ++kv) {
+      const unsigned char* src = c->host_kv + (size_t)kv * c->kv_bytes + (size_t)t0 * kKeyTile * kHeadDim * eb;
+      e = hipMemcpy2DAsync(stage[buf][kv], dst_pitch, src, src_pitch, (size_t)nt * kKeyTile * kHeadDim * eb,
+                           (size_t)BH, hipMemcpyHostToDevice, c->copy_stream);
+    }
+    if (e == hipSuccess) e = hipEventRecord(c->ev_ready[buf], c->copy_stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, c->ev_ready[buf], 0);
+    if (e != hipSuccess) break;
+    at.kc = stage[buf][0];
+    at.vt = stage[buf][1];
+    at.tile_base = t0;
+    at.split_base = i * c->chunk_splits;
+    {
+      TimedLaunch tl(SDM_ICL_TIMING_QUERY, s);
+      if (split) {
+        // launch only this chunk's splits: the grid's y extent is the chunk
+        AttnArgs ac = at;
+        const int nsplit = std::min(c->chunk_splits, c->splits - at.split_base);
+        e = launch_attention(ac, c->prec, true, s, nsplit);
+      } else {
+        e = launch_attention(at, c->prec, false, s);
+      }
+    }
+    if (e == hipSuccess) e = hipEventRecord(c->ev_free[buf], s);
+  }
+  if (e == hipSuccess && split) {
+    TimedLaunch tl(SDM_ICL_TIMING_COMBINE, s);
+    e = launch_combine(at.part_o, at.part_ml, c->scales + 2 * c->B * c->H, c->B, c->H, at.q_rows_valid,
+                       c->splits, c->prec, out, s);
+  }
+  return e;
 }
 
 }  // namespace
@@ -582,6 +712,11 @@ sdm_icl_status sdm_icl_attn_query(sdm_icl_cache c, const void* q, const void* ga
   at.out_rows = R;
   at.splits = c->splits;
   at.tiles_per_split = (int32_t)c->tiles_per_split;
+  if (c->offloaded) {
+    e = streamed_attention(c, at, w, L, (uint16_t*)out, s);
+    if (e != hipSuccess) return hip_fail(e, "query: streamed attention");
+    return SDM_ICL_OK;
+  }
   if (c->splits > 1) {
     at.part_o = (float*)(w + L.po_off);
     at.part_ml = (float*)(w + L.ml_off);
@@ -617,6 +752,8 @@ sdm_icl_status sdm_icl_attn_cache_info(sdm_icl_cache c, sdm_icl_cache_info* info
   info->keys_per_split = c->tiles_per_split * kKeyTile;
   info->length_scalar = c->L32[0];
   info->device_bytes = c->bytes;
+  info->offloaded = c->offloaded ? 1 : 0;
+  info->stream_chunk_splits = c->offloaded ? c->chunk_splits : 0;
   return SDM_ICL_OK;
 }
 
@@ -632,17 +769,25 @@ sdm_icl_status sdm_icl_attn_cache_export(sdm_icl_cache c, void* host_k, void* ho
   std::vector<unsigned char> tmp;
   hipError_t e = hipSuccess;
   if (host_k || host_v) tmp.resize(kv_bytes);
+  auto fetch = [&](int kv) {
+    if (c->offloaded) {
+      hipError_t e2 = hipStreamSynchronize(c->copy_stream);
+      std::memcpy(tmp.data(), c->host_kv + (size_t)kv * c->kv_bytes, kv_bytes);
+      return e2;
+    }
+    hipError_t e2 = hipMemcpyAsync(tmp.data(), kv ? c->vt : c->kc, kv_bytes, hipMemcpyDeviceToHost, s);
+    if (e2 == hipSuccess) e2 = hipStreamSynchronize(s);
+    return e2;
+  };
   if (host_k) {
-    e = hipMemcpyAsync(tmp.data(), c->kc, kv_bytes, hipMemcpyDeviceToHost, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    e = fetch(0);
     if (e != hipSuccess) return hip_fail(e, "cache_export: K copy");
     for (int64_t bh = 0; bh < BH; ++bh)
       std::memcpy((char*)host_k + bh * c->n_max * row_bytes, tmp.data() + bh * c->n_alloc * row_bytes,
                   (size_t)(c->n_max * row_bytes));
   }
   if (host_v) {
-    e = hipMemcpyAsync(tmp.data(), c->vt, kv_bytes, hipMemcpyDeviceToHost, s);
-    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    e = fetch(1);
     if (e != hipSuccess) return hip_fail(e, "cache_export: V copy");
     // tiles of [64 d][64 keys] -> rows [n][64 d]
     const int64_t tiles = c->n_alloc / kKeyTile;
@@ -759,9 +904,86 @@ sdm_icl_status sdm_icl_attn_release(sdm_icl_cache c) {
     g_registry.erase(c);
   }
   c->magic = 0;
-  hipError_t e = hipFreeAsync(c->block, c->stream);
+  hipError_t e = hipSuccess;
+  if (c->offloaded) {
+    // the copy stream may still be reading the pinned memory
+    e = hipStreamSynchronize(c->copy_stream);
+    hipError_t e2 = hipHostFree(c->host_kv);
+    if (e == hipSuccess) e = e2;
+    destroy_streaming(c);
+  }
+  hipError_t e3 = hipFreeAsync(c->block, c->stream);
+  if (e == hipSuccess) e = e3;
   delete c;
-  if (e != hipSuccess) return hip_fail(e, "release: hipFreeAsync");
+  if (e != hipSuccess) return hip_fail(e, "release");
+  return SDM_ICL_OK;
+}
+
+sdm_icl_status sdm_icl_attn_cache_offload(sdm_icl_cache c, size_t chunk_bytes, void* stream) {
+  if (!live(c)) return fail(SDM_ICL_E_STATE, "offload: unknown or released cache");
+  if (c->offloaded) return SDM_ICL_OK;
+  int dev;
+  DeviceInfo di;
+  sdm_icl_status st = current_device(&dev, &di);
+  if (st) return st;
+  if (dev != c->device) return fail(SDM_ICL_E_DEVICE, "offload: cache lives on device %d, current is %d", c->device, dev);
+  hipStream_t s = (hipStream_t)stream;
+  const size_t kv2 = 2 * c->kv_bytes, meta = c->bytes - kv2;
+  unsigned char* host = nullptr;
+  void* nb = nullptr;
+  hipError_t e = hipHostMalloc((void**)&host, kv2, hipHostMallocDefault);
+  if (e != hipSuccess) return hip_fail(e, "offload: pinned host allocation");
+  e = hipMallocAsync(&nb, meta, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(host, c->block, kv2, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(nb, (char*)c->block + kv2, meta, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = create_streaming(c, chunk_bytes);
+  if (e != hipSuccess) {
+    if (nb) (void)hipFreeAsync(nb, s);
+    (void)hipStreamSynchronize(s);
+    (void)hipHostFree(host);
+    return hip_fail(e, "offload");
+  }
+  (void)hipFreeAsync(c->block, s);
+  set_meta(c, nb);
+  c->block = nb;
+  c->kc = c->vt = nullptr;
+  c->bytes = meta;
+  c->host_kv = host;
+  c->offloaded = true;
+  return SDM_ICL_OK;
+}
+
+sdm_icl_status sdm_icl_attn_cache_restore(sdm_icl_cache c, void* stream) {
+  if (!live(c)) return fail(SDM_ICL_E_STATE, "restore: unknown or released cache");
+  if (!c->offloaded) return SDM_ICL_OK;
+  int dev;
+  DeviceInfo di;
+  sdm_icl_status st = current_device(&dev, &di);
+  if (st) return st;
+  if (dev != c->device) return fail(SDM_ICL_E_DEVICE, "restore: cache lives on device %d, current is %d", c->device, dev);
+  hipStream_t s = (hipStream_t)stream;
+  const size_t kv2 = 2 * c->kv_bytes, meta = c->bytes;
+  void* nb = nullptr;
+  hipError_t e = hipStreamSynchronize(c->copy_stream);
+  if (e == hipSuccess) e = hipMallocAsync(&nb, kv2 + meta, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(nb, c->host_kv, kv2, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipMemcpyAsync((char*)nb + kv2, c->block, meta, hipMemcpyDeviceToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) {
+    if (nb) (void)hipFreeAsync(nb, s);
+    return hip_fail(e, "restore");
+  }
+  (void)hipFreeAsync(c->block, s);
+  (void)hipHostFree(c->host_kv);
+  destroy_streaming(c);
+  c->kc = nb;
+  c->vt = (char*)nb + c->kv_bytes;
+  set_meta(c, (char*)nb + kv2);
+  c->block = nb;
+  c->bytes = kv2 + meta;
+  c->host_kv = nullptr;
+  c->offloaded = false;
   return SDM_ICL_OK;
 }
 
