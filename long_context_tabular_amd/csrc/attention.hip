@@ -317,6 +317,11 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
     ws.o[g][0] = f32x16{};
     ws.o[g][1] = f32x16{};
   }
+  // Wait here, once, for the Q fragments and scales.  Otherwise the wait the
+  // compiler places before their first use inside the tile loop covers every
+  // load then outstanding, including the K/V prefetch issued just before it,
+  // and each tile would stall on a full memory round trip.
+  __builtin_amdgcn_s_waitcnt(0);
 
   const int64_t n_tiles = (n + 63) / 64;
   const int64_t t0 = (int64_t)split * a.tiles_per_split;
@@ -394,18 +399,26 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
   // processed, the loads of tiles t+1 and t+2 are in flight.  Tile t+1 is
   // written to the other LDS buffers at the end of tile t (one barrier per
   // tile); the set it came from is then reloaded with tile t+3.
+  //
+  // Every load is issued on every path (past the end of the split they
+  // re-read its last tile), so the number of loads in flight is the same
+  // everywhere and the wait before a store leaves the other set's loads
+  // outstanding.
+  const int64_t t_last = t1 - 1;
+  auto clamp = [&](int64_t t) { return t < t_last ? t : t_last; };
   Stage<EB, R> sa, sb;
   load_stage(t0, sa);
   store_stage(0, sa);
-  if (t0 + 1 < t1) load_stage(t0 + 1, sa);
-  if (t0 + 2 < t1) load_stage(t0 + 2, sb);
+  load_stage(clamp(t0 + 1), sa);
+  load_stage(clamp(t0 + 2), sb);
   __syncthreads();
 
+  // tile t+1 goes from its staging set to LDS and the set is refilled with
+  // tile t+3 (both clamped to the range's last tile; past the end the copy
+  // lands in a buffer no later tile reads)
   auto advance = [&](int64_t t, Stage<EB, R>& next) {
-    if (t + 1 < t1) {
-      store_stage((int)((t + 1 - t0) & 1), next);
-      if (t + 3 < t1) load_stage(t + 3, next);
-    }
+    store_stage((int)((t + 1 - t0) & 1), next);
+    load_stage(clamp(t + 3), next);
     __syncthreads();
   };
   // tiles [t0, t_full) hold only valid keys; a partial tile can only be the
@@ -416,7 +429,7 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
     attend_tile<PREC, QG, true, false>(ws, kbuf[0], vbuf[0], c_scale, col, hf, 64);
   else
     attend_tile<PREC, QG, true, true>(ws, kbuf[0], vbuf[0], c_scale, col, hf, rem_last);
-  advance(t0, sa);
+  advance(t0, sa);  // for a one-tile range this stages an unused copy of the last tile
   // tile t0+1+2i takes its successor from sb, tile t0+2+2i from sa
   int64_t t = t0 + 1;
   for (; t + 1 < t_full; t += 2) {
