@@ -355,3 +355,41 @@ def context_outputs(cache: OracleCache, q: np.ndarray, gate: Optional[np.ndarray
         g = None if gate is None else gate[b, rows[valid]]
         out[valid] = attend(cache, q[b, rows[valid]], g, b=b, heads=heads)
     return out
+
+
+# ---------------------------------------------------------------------------
+# The shared Q/K/V projection, with the query scaling applied to its output
+# ("[FP8 3/4] Integrate FP8 attention and caching into TabICLv2", walkthrough:
+# shared attention projects Q/K/V before attending; "Fuse shared-length query
+# scaling during inference", Solution: the scaling joins the producer of q
+# instead of running as separate passes over it)
+# ---------------------------------------------------------------------------
+
+def project_qkv(x: np.ndarray, w: np.ndarray, bias: Optional[np.ndarray], heads: int,
+                head_dim: int) -> tuple:
+    """fp16 (Q, K, V), each ``[..., H, D]``, of hidden rows x ``[..., E]``.
+
+    w is ``[3 H D, E]`` (a linear layer's weight: the Q rows, then K, then V),
+    bias ``[3 H D]`` or None, both fp16.  Each output element is the sum
+    x . w_n + b_n taken in float64 (fp16 products are exact in it) and
+    rounded once to fp16 (nearest even).
+    """
+    x64 = np.asarray(x, dtype=np.float16).astype(np.float64)
+    w64 = np.asarray(w, dtype=np.float16).astype(np.float64)
+    y = x64 @ w64.T
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float16).astype(np.float64)
+    y16 = y.astype(np.float16)
+    hd = heads * head_dim
+    shape = x64.shape[:-1] + (heads, head_dim)
+    return (y16[..., :hd].reshape(shape), y16[..., hd:2 * hd].reshape(shape),
+            y16[..., 2 * hd:].reshape(shape))
+
+
+def project_scaled(x: np.ndarray, w: np.ndarray, bias: Optional[np.ndarray], heads: int,
+                   head_dim: int, mode: int, k_h: Optional[np.ndarray],
+                   gate: Optional[np.ndarray] = None) -> tuple:
+    """(q~, K, V): the projection with LogScale / GatedLogScale applied to its
+    fp16 Q output, exactly as the separate scaling pass would."""
+    q, k, v = project_qkv(x, w, bias, heads, head_dim)
+    return scale_queries(q, mode, k_h, gate), k, v

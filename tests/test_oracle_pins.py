@@ -314,6 +314,64 @@ def test_scoped_precision_is_the_intermediate_layer_rule():
     assert icl.fit(z, z, z, 8200, icl.SCALE_NONE, S).precision == F16
 
 
+def test_projection_layout_and_exact_sums():
+    """Weight rows are Q, then K, then V (a linear layer's [out, in] layout);
+    a scaled identity gives back x exactly; a bias alone comes through
+    rounded once; small-integer inputs give their exact integer sums."""
+    rng = np.random.default_rng(5)
+    H, D = 2, 64
+    E = H * D
+    x = (rng.standard_normal((3, 5, E)) / 4).astype(np.float16)
+    eye = np.eye(E)
+    w = np.concatenate([eye, 2 * eye, 0.5 * eye]).astype(np.float16)
+    q, k, v = icl.project_qkv(x, w, None, H, D)
+    want = x.reshape(3, 5, H, D)
+    np.testing.assert_array_equal(q, want)
+    np.testing.assert_array_equal(k, (2 * want.astype(np.float32)).astype(np.float16))
+    np.testing.assert_array_equal(v, (0.5 * want.astype(np.float32)).astype(np.float16))
+    b = (rng.standard_normal(3 * E) * 3).astype(np.float16)
+    q0, k0, v0 = icl.project_qkv(x, np.zeros_like(w), b, H, D)
+    np.testing.assert_array_equal(np.concatenate([q0[1, 2].ravel(), k0[1, 2].ravel(), v0[1, 2].ravel()]), b)
+    xi = rng.integers(-3, 4, size=(7, E))
+    wi = rng.integers(-3, 4, size=(3 * E, E))
+    bi = rng.integers(-50, 50, size=3 * E)
+    exact = xi @ wi.T + bi                                  # int64: |.| < 1200, exact in fp16
+    qi, ki, vi = icl.project_qkv(xi.astype(np.float16), wi.astype(np.float16), bi.astype(np.float16), H, D)
+    got = np.concatenate([qi.reshape(7, E), ki.reshape(7, E), vi.reshape(7, E)], axis=1)
+    np.testing.assert_array_equal(got.astype(np.int64), exact)
+
+
+def test_projection_rounds_once_to_nearest_even():
+    """1 + 2^-11 (exactly between fp16 1 and 1 + 2^-10) rounds to 1; adding
+    2^-30 rounds up.  A float32 intermediate would lose the 2^-30 and round
+    to 1 as well: the sum must be rounded once."""
+    E = 64
+    x = np.zeros((1, E), dtype=np.float16)
+    x[0, 0], x[0, 1], x[0, 2] = 1.0, 2.0 ** -11, 2.0 ** -15
+    w = np.zeros((3 * E, E), dtype=np.float16)
+    w[0, 0] = w[0, 1] = 1.0                  # q[0] = 1 + 2^-11: a tie, to even (1)
+    w[1, 0] = w[1, 1] = 1.0                  # q[1] = 1 + 2^-11 + 2^-30: above the tie
+    w[1, 2] = 2.0 ** -15
+    assert np.float32(1 + 2.0 ** -11) + np.float32(2.0 ** -30) == np.float32(1 + 2.0 ** -11)
+    q, _, _ = icl.project_qkv(x, w, None, 1, E)
+    assert q[0, 0, 0] == np.float16(1.0)
+    assert q[0, 0, 1] == np.float16(1.0 + 2.0 ** -10)
+
+
+def test_fused_projection_scaling_is_the_separate_pass():
+    rng = np.random.default_rng(6)
+    H, D, E = 2, 64, 96
+    x = (rng.standard_normal((4, E)) / 3).astype(np.float16)
+    w = (rng.standard_normal((3 * H * D, E)) / 8).astype(np.float16)
+    g = rng.standard_normal((4, H)).astype(np.float16)
+    kh = icl.head_factors(icl.length_scalar(5000), np.array([0.7, 1.3], dtype=np.float32))
+    q, k, v = icl.project_qkv(x, w, None, H, D)
+    qs, ks, vs = icl.project_scaled(x, w, None, H, D, icl.SCALE_GATED_LOG, kh, g)
+    np.testing.assert_array_equal(qs, icl.scale_queries(q, icl.SCALE_GATED_LOG, kh, g))
+    np.testing.assert_array_equal(ks, k)
+    assert not np.array_equal(qs, q)
+
+
 def test_fp8_is_lossless_on_grid_inputs():
     """I10: when Q~, K, V already lie on the e4m3 grid with amax = 448 s, FP8
     quantisation changes nothing and the FP8 result equals the FP16 one.  Each
