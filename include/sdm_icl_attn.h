@@ -234,6 +234,29 @@ sdm_icl_status sdm_icl_log_scale(const void* q, const void* gate, int32_t batch,
                                  const float* head_coef, int32_t scale_mode,
                                  const float* q_inv_scale, void* out, void* stream);
 
+/* The shared Q/K/V projection with the query scaling fused into its
+ * epilogue ("[FP8 3/4] ...", walkthrough: shared attention projects Q/K/V;
+ * "Fuse shared-length query scaling during inference", Solution: the scaling
+ * joins the producer of q instead of separate passes over it).
+ *   x:    device fp16 [B, rows, in_features] hidden rows (in_features % 32 == 0)
+ *   w:    device fp16 [3 * heads * head_dim, in_features]: a linear layer's
+ *         [out, in] weight, rows producing Q, then K, then V
+ *   bias: device fp16 [3 * heads * head_dim], or NULL
+ *   q_out, k_out, v_out: device fp16 [B, rows, heads, head_dim] (row-major, the
+ *         layout sdm_icl_attn_fit and sdm_icl_attn_query take)
+ * Each output is x . w_n + b_n accumulated in float32 and rounded once to
+ * fp16; q_out then takes scale_mode's scaling with key_length, head_coef and
+ * gate ([B, rows, heads], GATED_LOG only) exactly as sdm_icl_log_scale would
+ * apply it to the unscaled projection (bit for bit).  Rows projected this way
+ * already carry the scaling: fit and query them with SDM_ICL_SCALE_NONE.
+ * rows == 0 is a no-op.  Pointers as in the conventions above (x, w, outputs
+ * 16-byte aligned, bias and gate 2-byte aligned). */
+sdm_icl_status sdm_icl_qkv_project(const void* x, const void* w, const void* bias, int32_t batch,
+                                   int64_t rows, int32_t in_features, int32_t heads, int32_t head_dim,
+                                   int64_t key_length, const float* head_coef, int32_t scale_mode,
+                                   const void* gate, void* q_out, void* k_out, void* v_out,
+                                   void* stream);
+
 /* ---- kernel timing (observability) -------------------------------------
  * When enabled, each kernel launch of the library is bracketed by two HIP
  * events recorded on the launch's own stream, grouped by kernel class:
@@ -242,6 +265,7 @@ sdm_icl_status sdm_icl_log_scale(const void* q, const void* gate, int32_t batch,
  *   SDM_ICL_TIMING_COMBINE  split combine
  *   SDM_ICL_TIMING_SCALE    fused q-scale (+quantise)
  *   SDM_ICL_TIMING_PREP     fit preparation (amax, scales, K/V pack)
+ *   SDM_ICL_TIMING_PROJECT  Q/K/V projection (sdm_icl_qkv_project)
  * Off by default; enabling adds two event records per launch.
  * sdm_icl_timing_read waits for the recorded events of one class, returns
  * their summed duration in milliseconds and the launch count, and clears
@@ -251,6 +275,7 @@ sdm_icl_status sdm_icl_log_scale(const void* q, const void* gate, int32_t batch,
 #define SDM_ICL_TIMING_COMBINE 2
 #define SDM_ICL_TIMING_SCALE   3
 #define SDM_ICL_TIMING_PREP    4
+#define SDM_ICL_TIMING_PROJECT 5
 sdm_icl_status sdm_icl_timing_enable(int32_t on);
 sdm_icl_status sdm_icl_timing_read(int32_t kernel_class, double* total_ms, int64_t* launches);
 

@@ -84,6 +84,11 @@ _SIGNATURES = {
                                            ctypes.c_int64, ctypes.POINTER(ctypes.c_float),
                                            ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_void_p]),
+    "sdm_icl_qkv_project": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                             ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_int64, ctypes.POINTER(ctypes.c_float), ctypes.c_int32,
+                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p]),
     "sdm_icl_timing_enable": (ctypes.c_int32, [ctypes.c_int32]),
     "sdm_icl_timing_read": (ctypes.c_int32, [ctypes.c_int32, ctypes.POINTER(ctypes.c_double),
                                              ctypes.POINTER(ctypes.c_int64)]),
@@ -233,7 +238,7 @@ def sdm_icl_split_plan(n: int, num_cus: int, bh_count: int):
 
 
 SDM_ICL_TIMING_CONTEXT, SDM_ICL_TIMING_QUERY, SDM_ICL_TIMING_COMBINE = 0, 1, 2
-SDM_ICL_TIMING_SCALE, SDM_ICL_TIMING_PREP = 3, 4
+SDM_ICL_TIMING_SCALE, SDM_ICL_TIMING_PREP, SDM_ICL_TIMING_PROJECT = 3, 4, 5
 
 
 def sdm_icl_timing_enable(on: bool) -> None:
@@ -437,3 +442,32 @@ def sdm_icl_log_scale(q, key_length: int, head_coef=None, scale_mode: int = SDM_
                                    _dev_ptr(q_inv_scale, "q_inv_scale", torch.float32),
                                    _dev_ptr(out, "out"), _stream_ptr(stream)))
     return out
+
+
+def sdm_icl_qkv_project(x, w, bias=None, heads: int = 8, key_length: int = 0, head_coef=None,
+                        scale_mode: int = SDM_ICL_SCALE_NONE, gate=None, outs=None, stream=None):
+    """(q~, k, v) ``[B, rows, H, 64]`` fp16 of hidden rows x ``[B, rows, E]`` and a
+    linear layer's weight w ``[3 H 64, E]`` (Q rows, then K, then V), bias
+    ``[3 H 64]`` or None; q~ carries ``scale_mode``'s scaling."""
+    import torch
+    B, R, E = x.shape
+    D = 64
+    if tuple(w.shape) != (3 * heads * D, E):
+        raise ValueError("w must be [3 * heads * 64, in_features]")
+    if bias is not None and tuple(bias.shape) != (3 * heads * D,):
+        raise ValueError("bias must be [3 * heads * 64]")
+    if gate is not None and tuple(gate.shape) != (B, R, heads):
+        raise ValueError("gate must be [B, rows, heads]")
+    if outs is None:
+        outs = tuple(torch.empty((B, R, heads, D), dtype=torch.float16, device=x.device) for _ in range(3))
+    coef = None
+    coef_np = None
+    if head_coef is not None:
+        coef_np = np.ascontiguousarray(head_coef, dtype=np.float32)
+        coef = coef_np.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    f16 = torch.float16
+    _check(lib().sdm_icl_qkv_project(_dev_ptr(x, "x", f16), _dev_ptr(w, "w", f16), _dev_ptr(bias, "bias", f16),
+                                     B, R, E, heads, D, int(key_length), coef, scale_mode,
+                                     _dev_ptr(gate, "gate", f16), *(_dev_ptr(o, "out", f16) for o in outs),
+                                     _stream_ptr(stream)))
+    return outs

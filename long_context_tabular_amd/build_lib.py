@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_NAME = "libsdm_icl_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["prep.hip", "attention.hip", "sdm_icl_attn.cpp"]
+SOURCES = ["prep.hip", "attention.hip", "projection.hip", "sdm_icl_attn.cpp"]
 # per-source flags: the attention kernels schedule for instruction-level
 # parallelism (measured ~5% faster on the 512K context pass)
 EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}

@@ -19,6 +19,7 @@
 #include <stdint.h>
 
 #include "internal.h"
+#include "scaling.h"
 
 namespace sdm {
 namespace {
@@ -26,42 +27,6 @@ namespace {
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// ---------------------------------------------------------------- scalar math
-
-// Correctly rounded double -> fp16: round to odd into float (the sticky bit
-// keeps the information a second rounding needs; float has >= 2 more bits than
-// fp16), then round to nearest even into fp16.
-__device__ inline _Float16 f64_to_f16(double d) {
-  float f = (float)d;
-  const double df = (double)f;
-  if (df != d) {
-    uint32_t b = __float_as_uint(f);
-    if (fabs(df) > fabs(d)) b -= 1u;  // step one ulp towards zero (f != 0 here)
-    f = __uint_as_float(b | 1u);
-  }
-  return (_Float16)f;
-}
-
-// fp16(1 + fp16(tanh g)) as a float; tanh is evaluated in double so the fp16
-// result is the correctly rounded one.
-__device__ inline float gate_factor(_Float16 g) {
-  const _Float16 t = f64_to_f16(tanh((double)g));
-  return (float)(_Float16)(1.0f + (float)t);
-}
-
-// One element of q~: NONE q, LOG fp16(q*k), GATED fp16(fp16(q*k)*u).  The
-// fp16 x fp16 products are exact in float32, so each step rounds once.
-template <int MODE>
-__device__ inline _Float16 scale_elem(_Float16 q, float kh, float u) {
-  if constexpr (MODE == kScaleNone) {
-    return q;
-  } else {
-    const _Float16 qk = (_Float16)((float)q * kh);
-    if constexpr (MODE == kScaleLog) return qk;
-    return (_Float16)((float)qk * u);
-  }
-}
 
 // e4m3 codes of two values (clamped to +-448 first; the hardware conversion
 // rounds to nearest even, first operand in byte 0).

@@ -194,7 +194,7 @@ bool live(const sdm_icl_cache_s* c) {
 }
 
 // ---- kernel timing: event pairs around launches, per kernel class
-constexpr int kTimingClasses = 5;
+constexpr int kTimingClasses = 6;
 struct TimingRec {
   int cls;
   hipEvent_t a, b;
@@ -1056,6 +1056,56 @@ sdm_icl_status sdm_icl_log_scale(const void* q, const void* gate, int32_t batch,
   hipError_t e = launch_scale_queries((const uint16_t*)q, (const uint16_t*)gate, batch, rows, rows, nullptr,
                                       rows, heads, scale_mode, fac, q_inv_scale, out, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "log_scale: launch");
+  return SDM_ICL_OK;
+}
+
+sdm_icl_status sdm_icl_qkv_project(const void* x, const void* w, const void* bias, int32_t batch,
+                                   int64_t rows, int32_t in_features, int32_t heads, int32_t head_dim,
+                                   int64_t key_length, const float* head_coef, int32_t scale_mode,
+                                   const void* gate, void* q_out, void* k_out, void* v_out,
+                                   void* stream) {
+  if (batch < 1 || rows < 0 || heads < 1) return fail(SDM_ICL_E_INVALID, "qkv_project: bad shape");
+  if (heads > kMaxHeads) return fail(SDM_ICL_E_UNSUPPORTED, "qkv_project: at most %d heads", kMaxHeads);
+  if (head_dim != kHeadDim) return fail(SDM_ICL_E_UNSUPPORTED, "qkv_project: head_dim must be 64");
+  if (in_features < 32 || in_features % 32 != 0)
+    return fail(SDM_ICL_E_UNSUPPORTED, "qkv_project: in_features must be a positive multiple of 32 (got %d)", in_features);
+  if (key_length < 0) return fail(SDM_ICL_E_INVALID, "qkv_project: key_length < 0");
+  if (scale_mode < SDM_ICL_SCALE_NONE || scale_mode > SDM_ICL_SCALE_GATED_LOG)
+    return fail(SDM_ICL_E_INVALID, "qkv_project: unknown scale_mode %d", scale_mode);
+  if ((gate != nullptr) != (scale_mode == SDM_ICL_SCALE_GATED_LOG))
+    return fail(SDM_ICL_E_INVALID, "qkv_project: gate must be given exactly when scale_mode is GATED_LOG");
+  if ((head_coef != nullptr) != (scale_mode != SDM_ICL_SCALE_NONE))
+    return fail(SDM_ICL_E_INVALID, "qkv_project: head_coef must be given exactly when scale_mode is LOG or GATED_LOG");
+  if (rows == 0) return SDM_ICL_OK;
+  if (!x || !w || !q_out || !k_out || !v_out)
+    return fail(SDM_ICL_E_INVALID, "qkv_project: x, w and the three outputs are required");
+  if ((int64_t)batch * rows > ((int64_t)1 << 31) * kQueryPad)
+    return fail(SDM_ICL_E_INVALID, "qkv_project: too many rows");
+  {
+    const void* p16[] = {x, w, q_out, k_out, v_out};
+    const char* n16[] = {"x", "w", "q_out", "k_out", "v_out"};
+    for (int i = 0; i < 5; ++i)
+      if (!aligned(p16[i], 16)) return fail(SDM_ICL_E_INVALID, "qkv_project: %s must be 16-byte aligned", n16[i]);
+    if (!aligned(bias, 2) || !aligned(gate, 2))
+      return fail(SDM_ICL_E_INVALID, "qkv_project: bias and gate must be 2-byte aligned");
+  }
+  int dev;
+  DeviceInfo di;
+  sdm_icl_status st = current_device(&dev, &di);
+  if (st) return st;
+  const void* ptrs[] = {x, w, bias, gate, q_out, k_out, v_out};
+  const char* names[] = {"x", "w", "bias", "gate", "q_out", "k_out", "v_out"};
+  for (int i = 0; i < 7; ++i)
+    if (ptrs[i] && (st = check_device_ptr(ptrs[i], dev, names[i]))) return st;
+  HeadFactors kh;
+  if (scale_mode != SDM_ICL_SCALE_NONE) head_factors(key_length, head_coef, heads, &kh);
+  else std::memset(&kh, 0, sizeof kh);
+  TimedLaunch tl(SDM_ICL_TIMING_PROJECT, (hipStream_t)stream);
+  hipError_t e = launch_qkv_project((const uint16_t*)x, (const uint16_t*)w, (const uint16_t*)bias,
+                                    (int64_t)batch * rows, in_features, heads, scale_mode, kh,
+                                    (const uint16_t*)gate, (uint16_t*)q_out, (uint16_t*)k_out,
+                                    (uint16_t*)v_out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "qkv_project: launch");
   return SDM_ICL_OK;
 }
 

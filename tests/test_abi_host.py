@@ -303,3 +303,26 @@ def test_import_accepts_the_scale_of_every_fp16_amax():
 def _all_finite_fp16_positive():
     v = np.arange(1, 0x7C00, dtype=np.uint16).view(np.float16)
     return v[v > 0]
+
+
+# ----------------------------------------------------------------- projection (host validation)
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(in_features=48), 2),                 # not a multiple of 32
+    (dict(head_dim=128), 2),
+    (dict(heads=0), 1),
+    (dict(scale_mode=1), 1),                   # LOG without coefficients
+    (dict(scale_mode=0, gate=0x7000), 1),      # gate without GATED
+    (dict(x=0x1008), 1),                       # misaligned
+    (dict(q_out=None), 1),
+    (dict(key_length=-1), 1),
+])
+def test_projection_rejects_bad_arguments(kw, status):
+    a = dict(x=0x1000, w=0x2000, bias=None, batch=1, rows=10, in_features=64, heads=2, head_dim=64,
+             key_length=100, head_coef=None, scale_mode=0, gate=None, q_out=0x3000, k_out=0x4000,
+             v_out=0x5000, stream=None)
+    a.update(kw)
+    st = B.lib().sdm_icl_qkv_project(a["x"], a["w"], a["bias"], a["batch"], a["rows"], a["in_features"],
+                                      a["heads"], a["head_dim"], a["key_length"], a["head_coef"],
+                                      a["scale_mode"], a["gate"], a["q_out"], a["k_out"], a["v_out"], a["stream"])
+    assert st == status, B.sdm_icl_last_error()
