@@ -205,6 +205,39 @@ def bench_cached(B, gen, w, reps, offload=True):
     return res, info
 
 
+def bench_projection(B, w, reps: int = 5):
+    """The fused Q/K/V projection at the model-call size: hidden rows
+    [1, n_pad, H*64] times a [3*H*64, H*64] weight, LogScale on Q."""
+    import numpy as np
+    import torch
+    g = torch.Generator(device="cuda").manual_seed(w.seed)
+    E = w.heads * w.head_dim
+    x = (torch.randn((1, w.n_pad, E), generator=g, device="cuda") / 2).half()
+    wt = (torch.randn((3 * E, E), generator=g, device="cuda") / (4 * E ** 0.5)).half()
+    bias = (torch.randn((3 * E,), generator=g, device="cuda") / 16).half()
+    coef = np.linspace(0.5, 1.5, w.heads).astype(np.float32)
+    outs = tuple(torch.empty((1, w.n_pad, w.heads, w.head_dim), dtype=torch.float16, device="cuda") for _ in range(3))
+    run = lambda: B.sdm_icl_qkv_project(x, wt, bias, heads=w.heads, key_length=w.n_valid, head_coef=coef,
+                                        scale_mode=B.SDM_ICL_SCALE_LOG, outs=outs)
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)[reps // 2]
+    flops = 2.0 * w.n_pad * 3 * E * E
+    hbm = (w.n_pad * E + 3 * E * E + 3 * w.n_pad * E) * 2
+    return {"rows": w.n_pad, "in_features": E, "out_features": 3 * E, "ms": round(ms, 4),
+            "TFLOP_per_s": round(flops / (ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4),
+            "GB_per_s": round(hbm / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(hbm / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+
+
 def cpu_baseline(gen, x, w, sample_rows: int):
     """The float64 oracle (as it stands) on a bounded sample of the same workload."""
     import numpy as np
@@ -245,6 +278,8 @@ def main() -> int:
     ap.add_argument("--cached-reps", type=int, default=30)
     ap.add_argument("--no-cached", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-projection", action="store_true",
+                    help="skip timing the fused Q/K/V projection")
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the host-offloaded (PCIe-streamed) cached queries")
     ap.add_argument("--no-model-call", action="store_true",
@@ -333,6 +368,9 @@ def main() -> int:
                                                for kk, vv in v.items()} for k, v in cres.items()},
                           "offloaded": cinfo.get("offloaded_queries")}
         log(f"[bench] cached: {json.dumps(line['cached'])}")
+    if not args.no_projection:
+        line["projection"] = bench_projection(B, w)
+        log(f"[bench] projection: {json.dumps(line['projection'])}")
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (float64 oracle)")
         line["cpu_baseline"] = cpu_baseline(gen, x, w, args.cpu_sample_rows)

@@ -15,9 +15,9 @@
 // 64 x 64 as 2 x 2 tiles of v_mfma_f32_32x32x16_f16.  Both operands are
 // K-contiguous, so the x and w tiles are staged into LDS the same way (rows of
 // 32 halves padded to 40), the next K step is loaded into registers while the
-// current one is multiplied, one barrier per step.  The grid runs the output
-// column tiles fastest so the blocks of one row tile follow each other and
-// share it in L2.
+// current one is multiplied, one barrier per step.  Workgroups are mapped to
+// tiles so that the column tiles of one row tile run back to back on one XCD
+// and share the row tile in that XCD's L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -32,40 +32,70 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 128, kBN = 128, kBK = 32;
-constexpr int kLRow = 40;  // LDS halves per staged row (32 + 8 pad)
+constexpr int kDepth = 3;   // K steps loaded ahead into registers
+constexpr int kLRow = 40;   // LDS halves per staged row (32 + 8 pad)
+constexpr int kCRow = 136;  // LDS halves per row of the output tile (128 + 8 pad)
+constexpr int kSmem = 2 * (kBM + kBN) * kLRow;  // operand stages; the output tile reuses them
+static_assert(kBM * kCRow <= kSmem, "output tile must fit in the operand stages");
 
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void qkv_project_kernel(
     const _Float16* __restrict__ x, const _Float16* __restrict__ w, const _Float16* __restrict__ bias,
     int64_t M, int N, int K, int HD, int H, HeadFactors kh, const _Float16* __restrict__ gate,
     _Float16* __restrict__ q_out, _Float16* __restrict__ k_out, _Float16* __restrict__ v_out) {
-  __shared__ __attribute__((aligned(16))) _Float16 as[2][kBM * kLRow];
-  __shared__ __attribute__((aligned(16))) _Float16 bs[2][kBN * kLRow];
+  __shared__ __attribute__((aligned(16))) _Float16 smem[kSmem];
+  auto as = [&](int buf) { return smem + buf * kBM * kLRow; };
+  auto bs = [&](int buf) { return smem + 2 * kBM * kLRow + buf * kBN * kLRow; };
   __shared__ float gate_u[kBM][2];  // gate factors of the tile's rows for its (at most) two heads
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int wm = wv >> 1, wn = wv & 1;
-  const int n0 = blockIdx.x * kBN;
-  const int64_t m0 = (int64_t)blockIdx.y * kBM;
+  // XCD-aware tile order: workgroups are handed to the 8 XCDs round-robin, so
+  // workgroup L runs on XCD L % 8.  XCD j takes the row tiles j, j + 8, ...
+  // and runs all column tiles of one row tile back to back, which then share
+  // that x tile in its L2; the rows past the last full group of 8 follow in
+  // plain row-major order.
+  const int ctiles = (N + kBN - 1) / kBN;
+  const int64_t rtiles = (M + kBM - 1) / kBM, rfull = rtiles / 8 * 8;
+  const int64_t L = blockIdx.x;
+  int64_t rt, ct_;
+  if (L < rfull * ctiles) {
+    const int64_t k = L / 8;
+    rt = L % 8 + 8 * (k / ctiles);
+    ct_ = k % ctiles;
+  } else {
+    const int64_t u = L - rfull * ctiles;
+    rt = rfull + u / ctiles;
+    ct_ = u % ctiles;
+  }
+  const int n0 = (int)ct_ * kBN;
+  const int64_t m0 = rt * kBM;
 
-  // staging chunk c = tid + 256 i: row c / 4 of the tile, 8 halves at k (c % 4) * 8
-  i32x4 ra[2], rb[2];
-  auto load = [&](int k0) {
+  // staging chunk c = tid + 256 i: row c / 4 of the tile, 8 halves at k (c % 4) * 8;
+  // kDepth register sets hold the next K steps in flight
+  struct St { i32x4 a[2], b[2]; };
+  St ring[kDepth];
+  const int nk = K / kBK;
+  auto load = [&](int kt, St& st) {
+    const int k0 = (kt < nk ? kt : nk - 1) * kBK;  // past the end: re-read the last step (unused)
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int c = tid + 256 * i, r = c >> 2, kq = c & 3;
+      // rows past the end re-read the last row: every load is issued (a
+      // static count of loads in flight), and those rows only reach outputs
+      // past the end, which are never stored
       const int64_t m = m0 + r;
       const int n = n0 + r;
-      ra[i] = m < M ? *reinterpret_cast<const i32x4*>(x + m * K + k0 + kq * 8) : i32x4{0, 0, 0, 0};
-      rb[i] = n < N ? *reinterpret_cast<const i32x4*>(w + (int64_t)n * K + k0 + kq * 8) : i32x4{0, 0, 0, 0};
+      st.a[i] = *reinterpret_cast<const i32x4*>(x + (m < M ? m : M - 1) * K + k0 + kq * 8);
+      st.b[i] = *reinterpret_cast<const i32x4*>(w + (int64_t)(n < N ? n : N - 1) * K + k0 + kq * 8);
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int buf, const St& st) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int c = tid + 256 * i, r = c >> 2, kq = c & 3;
-      *reinterpret_cast<i32x4*>(&as[buf][r * kLRow + kq * 8]) = ra[i];
-      *reinterpret_cast<i32x4*>(&bs[buf][r * kLRow + kq * 8]) = rb[i];
+      *reinterpret_cast<i32x4*>(&as(buf)[r * kLRow + kq * 8]) = st.a[i];
+      *reinterpret_cast<i32x4*>(&bs(buf)[r * kLRow + kq * 8]) = st.b[i];
     }
   };
 
@@ -85,55 +115,86 @@ __global__ __launch_bounds__(256, 2) void qkv_project_kernel(
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  load(0);
-  store(0);
+  // step kt is multiplied from LDS buffer kt % 2 while steps kt+1 .. kt+kDepth
+  // are in flight in the register ring (slot (kt+1) % kDepth is stored at the
+  // end of step kt and refilled with step kt+1+kDepth)
+  load(0, ring[0]);
+  store(0, ring[0]);
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) load(1 + d, ring[d]);
   __syncthreads();
-  const int nk = K / kBK;
-  for (int kt = 0; kt < nk; ++kt) {
+  auto step = [&](int kt, St& next) {
     const int buf = kt & 1;
-    if (kt + 1 < nk) load((kt + 1) * kBK);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       f16x8 a[2], b[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        a[t] = *reinterpret_cast<const f16x8*>(&as[buf][(wm * 64 + t * 32 + (lane & 31)) * kLRow + kk * 16 + 8 * (lane >> 5)]);
-        b[t] = *reinterpret_cast<const f16x8*>(&bs[buf][(wn * 64 + t * 32 + (lane & 31)) * kLRow + kk * 16 + 8 * (lane >> 5)]);
+        a[t] = *reinterpret_cast<const f16x8*>(&as(buf)[(wm * 64 + t * 32 + (lane & 31)) * kLRow + kk * 16 + 8 * (lane >> 5)]);
+        b[t] = *reinterpret_cast<const f16x8*>(&bs(buf)[(wn * 64 + t * 32 + (lane & 31)) * kLRow + kk * 16 + 8 * (lane >> 5)]);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) store(buf ^ 1);
+    if (kt + 1 < nk) store(buf ^ 1, next);
+    // issued on every step (clamped past the end) so that the number of
+    // loads in flight is the same on every path and the wait before a store
+    // covers only that store's own step
+    load(kt + 1 + kDepth, next);
     __syncthreads();
+  };
+  // the ring slot of step kt+1 is (kt % kDepth): unrolled by kDepth so that
+  // every slot index is a constant
+  int kt = 0;
+  for (; kt + kDepth <= nk; kt += kDepth) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) step(kt + d, ring[d]);
   }
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d)
+    if (kt + d < nk) step(kt + d, ring[d]);
 
-  // ---- epilogue: lane holds column n = ... + lane % 32 of 16 rows per tile
+  // ---- epilogue.  Each lane holds column wn*64 + j*32 + lane%32 of 16 rows
+  // per tile: bias, one fp16 rounding and the Q scaling are applied there and
+  // the tile is assembled in LDS (the operand stages are free after the last
+  // barrier), then written out as 16-byte row segments.
+  _Float16* const ct = smem;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int n = n0 + wn * 64 + j * 32 + (lane & 31);
-    if (n >= N) continue;
-    const int t = n / HD, c = n - t * HD;
-    _Float16* out = t == 0 ? q_out : (t == 1 ? k_out : v_out);
-    const float bn = bias ? (float)bias[n] : 0.f;
-    const int head = c >> 6;  // head_dim 64
-    const float kf = (float)__builtin_bit_cast(_Float16, kh.bits[head < kMaxHeads ? head : 0]);
+    const int cc = wn * 64 + j * 32 + (lane & 31);
+    const int n = n0 + cc;
+    const int nn = n < N ? n : N - 1;
+    const int t = nn / HD, c = nn - t * HD;
+    const float bn = bias ? (float)bias[nn] : 0.f;
+    const float kf = (float)__builtin_bit_cast(_Float16, kh.bits[(c >> 6) < kMaxHeads ? (c >> 6) : 0]);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int rr = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int64_t m = m0 + rr;
-        if (m >= M) continue;
         _Float16 y = (_Float16)(acc[i][j][r] + bn);
         if (t == 0) {
           float u = 1.0f;
           if constexpr (MODE == kScaleGated) u = gate_u[rr][(c >> 6) - n0 / 64];
           y = scale_elem<MODE>(y, kf, u);
         }
-        out[m * HD + c] = y;
+        ct[rr * kCRow + cc] = y;
       }
+  }
+  __syncthreads();
+  // 128 rows x 16 segments of 8 halves; a segment never straddles two
+  // tensors (H*64 is a multiple of 8)
+#pragma unroll
+  for (int p = 0; p < (kBM * kBN / 8) / 256; ++p) {
+    const int q = tid + 256 * p, row = q >> 4, c8 = q & 15;
+    const int64_t m = m0 + row;
+    const int n = n0 + c8 * 8;
+    if (m >= M || n >= N) continue;
+    const int t = n / HD, c = n - t * HD;
+    _Float16* out = t == 0 ? q_out : (t == 1 ? k_out : v_out);
+    *reinterpret_cast<i32x4*>(out + m * HD + c) = *reinterpret_cast<const i32x4*>(&ct[row * kCRow + c8 * 8]);
   }
 }
 
@@ -143,7 +204,7 @@ hipError_t launch_qkv_project(const uint16_t* x, const uint16_t* w, const uint16
                               int K, int H, int mode, const HeadFactors& kh, const uint16_t* gate,
                               uint16_t* q_out, uint16_t* k_out, uint16_t* v_out, hipStream_t s) {
   const int HD = H * kHeadDim, N = 3 * HD;
-  const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM));
+  const dim3 grid((unsigned)(((N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM)));
   auto xp = reinterpret_cast<const _Float16*>(x);
   auto wp = reinterpret_cast<const _Float16*>(w);
   auto bp = reinterpret_cast<const _Float16*>(bias);
