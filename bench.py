@@ -38,7 +38,7 @@ def log(*a):
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("attention.hip", "prep.hip"):
+    for f in ("attention.hip", "prep.hip", "scaling.h"):
         with open(os.path.join(ROOT, "long_context_tabular_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
