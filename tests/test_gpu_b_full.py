@@ -80,8 +80,18 @@ def test_full_cached512k_fp8_gated():
     parts = np.concatenate([r.query(cache, (i, i + 128)).cpu().numpy() for i in range(0, 1024, 128)], axis=1)
     torch.cuda.synchronize()
     _, _, sc = B.sdm_icl_attn_cache_export(cache)
+    # the same queries with the cache offloaded to host memory and streamed
+    # back in chunks (default chunk size): bit-identical
+    B.sdm_icl_attn_cache_offload(cache)
+    info = cache.info()
+    say(f"  offloaded: {info['stream_chunk_splits']} of {info['kv_splits']} splits per chunk")
+    streamed = r.query(cache).cpu().numpy()
+    streamed128 = r.query(cache, (384, 512)).cpu().numpy()
     cache.release()
+    assert info["offloaded"] == 1 and info["stream_chunk_splits"] < info["kv_splits"]
     np.testing.assert_array_equal(full.view(np.uint16), parts.view(np.uint16))
+    np.testing.assert_array_equal(full.view(np.uint16), streamed.view(np.uint16))
+    np.testing.assert_array_equal(full[:, 384:512].view(np.uint16), streamed128.view(np.uint16))
     np.testing.assert_array_equal(sc, r.oracle.scales)
     rows = np.concatenate([np.arange(4), np.arange(1020, 1024), np.arange(127, 1024, 113)])
     _check(r, None, full, [], np.unique(rows))
@@ -103,3 +113,27 @@ def test_full_model512k_fp8_log():
     assert info["n_valid"] == 523288 and info["length_scalar"] == r.oracle.L32
     assert np.all(out[0, w.n_valid:] == 0)
     _check(r, out, oq.cpu().numpy(), gen.sample_rows(w.n_valid, 24, w.seed), np.arange(0, 1024, 64))
+
+
+@pytest.mark.timeout(300)
+def test_full_ragged_two_contexts_in_one_cache():
+    """Two batch elements with 524,288 and 300,001 valid rows in one fit and
+    one query launch (per-batch lengths, FP8, GatedLogScale, outliers, NaN
+    tails): sampled parity per element, each against all of its keys."""
+    import torch
+    from dataclasses import replace
+    w = replace(gen.WORKLOADS["cached512k_fp8_gated"], name="ragged512k", seed=61, batch=2,
+                lengths=(524288, 300001), n_query=256, nan_tail=True)
+    r = Run(w)
+    say("full ragged 524,288 + 300,001")
+    cache, _ = r.fit(out_ctx=False)
+    oq = r.query(cache).cpu().numpy()
+    n_b, L = B.sdm_icl_attn_cache_lengths(cache)
+    cache.release()
+    assert list(n_b) == [524288, 300001]
+    np.testing.assert_array_equal(L, r.oracle.L32s)
+    rows = np.unique(np.concatenate([np.arange(4), np.arange(252, 256), np.arange(5, 256, 41)]))
+    for b in range(2):
+        e = norm_err(oq[b, rows].astype(np.float64), r.ref_query(rows, b=b))
+        say(f"  b={b}: query err {e:.3e}")
+        assert e <= TOL[w.precision]
