@@ -14,8 +14,8 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests run in one process on the GPU machine; on a host without a GPU
-    # they are skipped rather than failed so that "-m 'not gpu'" stays green.
+    # GPU tests run in one process on a machine with an MI355X; on a host
+    # without a GPU they are skipped rather than failed.
     try:
         import torch
         has_gpu = torch.cuda.is_available()
