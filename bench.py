@@ -284,7 +284,7 @@ def main() -> int:
                     help="skip the host-offloaded (PCIe-streamed) cached queries")
     ap.add_argument("--no-model-call", action="store_true",
                     help="skip the model-call measurement (only the cached-prediction leg runs)")
-    ap.add_argument("--cpu-sample-rows", type=int, default=128)
+    ap.add_argument("--cpu-sample-rows", type=int, default=384)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times) and exit; "
                          "the reference for scaling FETCH_SIZE / WRITE_SIZE counters")
