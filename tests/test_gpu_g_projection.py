@@ -92,3 +92,63 @@ def test_projected_rows_feed_fit_and_query():
     e_q = norm_err(oq.cpu().numpy()[0], icl.attend(o, rq[0, n:], None))
     say(f"projected rows: context err {e_ctx:.2e}, query err {e_q:.2e}")
     assert e_ctx <= TOL[B.SDM_ICL_PREC_FP8_E4M3] and e_q <= TOL[B.SDM_ICL_PREC_FP8_E4M3]
+
+
+def _check_unscaled_and_scaled(xd, wd, bd, gd, H, key_length, c, mode, rows=None, ref_rows=None, g=None):
+    """The unscaled projection within one fp16 ulp of the oracle's (on `rows`
+    or all rows), and the fused scaling bit-identical to the oracle's scaling
+    of the kernel's own unscaled Q; K and V identical in both calls.  (A
+    one-ulp difference of a subnormal unscaled value becomes many ulps of the
+    scaled one, so the scaled output is compared on equal inputs.)"""
+    import torch
+    q0, k0, v0 = B.sdm_icl_qkv_project(xd, wd, bd, heads=H)
+    q1, k1, v1 = B.sdm_icl_qkv_project(xd, wd, bd, heads=H, key_length=key_length,
+                                       head_coef=c if mode != icl.SCALE_NONE else None, scale_mode=mode, gate=gd)
+    torch.cuda.synchronize()
+    sel = (lambda t: t[0, torch.from_numpy(rows).cuda()].cpu().numpy()[None]) if rows is not None else \
+          (lambda t: t.cpu().numpy())
+    for got, want in zip((q0, k0, v0), ref_rows):
+        got = sel(got)
+        diff = np.abs(got.astype(np.float32) - want.astype(np.float32))
+        assert np.all(diff <= _ulp16(want) * 1.0001), float(diff.max())
+        same = np.mean(got == want)
+        say(f"  identical fraction {same:.5f}")
+        assert same > 0.99
+    np.testing.assert_array_equal(sel(k1), sel(k0))
+    np.testing.assert_array_equal(sel(v1), sel(v0))
+    kh = icl.head_factors(icl.length_scalar(key_length), c)
+    gs = g if (g is None or rows is None) else g[:, rows]
+    np.testing.assert_array_equal(sel(q1), icl.scale_queries(sel(q0), mode, kh, gs if gd is not None else None))
+
+
+@pytest.mark.parametrize("R,E,H,mode", [(76833, 64, 8, icl.SCALE_LOG),      # 2 K steps: ring spans tiles
+                                        (40001, 96, 3, icl.SCALE_GATED_LOG),  # 3 K steps, ragged N
+                                        (30000, 32, 2, icl.SCALE_NONE)])      # 1 K step
+def test_projection_many_tiles_per_workgroup(R, E, H, mode):
+    """More output tiles than workgroups, so each workgroup walks several
+    tiles and its load ring crosses tile boundaries; K of 1 to 3 steps of 32
+    (fewer than or as many as the ring holds); ragged rows and features."""
+    x, w, b, g, c = _data(1, R, E, H, 54)
+    say("projection many tiles", R, E, H, mode)
+    gd = to_dev(g) if mode == icl.SCALE_GATED_LOG else None
+    _check_unscaled_and_scaled(to_dev(x), to_dev(w), to_dev(b), gd, H, R, c, mode,
+                               ref_rows=icl.project_qkv(x, w, b, H, 64), g=g)
+
+
+def test_projection_full_size_sampled_rows():
+    """The benchmark's shape (524,288 hidden rows of 512 features, 8 heads,
+    LogScale) in the benchmark's launch, checked on sampled rows (first and
+    last rows of the range and seeded random ones) against the oracle's
+    projection of those rows."""
+    import torch
+    M, E, H = 524288, 512, 8
+    gen_t = torch.Generator(device="cuda").manual_seed(55)
+    x = (torch.randn((1, M, E), generator=gen_t, device="cuda") / 2).half()
+    wt = (torch.randn((3 * H * 64, E), generator=gen_t, device="cuda") / (4 * E ** 0.5)).half()
+    bias = (torch.randn((3 * H * 64,), generator=gen_t, device="cuda") / 16).half()
+    c = np.linspace(0.5, 1.5, H).astype(np.float32)
+    rows = gen.sample_rows(M, 96, 56)
+    xs = x[0, torch.from_numpy(rows).cuda()].cpu().numpy()[None]
+    ref = icl.project_qkv(xs, wt.cpu().numpy(), bias.cpu().numpy(), H, 64)
+    say("projection full size")
+    _check_unscaled_and_scaled(x, wt, bias, None, H, M - 1000, c, icl.SCALE_LOG, rows=rows, ref_rows=ref)
