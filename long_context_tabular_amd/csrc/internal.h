@@ -98,11 +98,9 @@ hipError_t launch_combine(const float* part_o, const float* part_ml, const float
 // Q/K/V projection x [M][K] (fp16) times w [3*H*64][K] (fp16, a linear layer's
 // [out, in] layout) plus bias [3*H*64] (fp16, may be NULL), rounded once to
 // fp16 into q_out / k_out / v_out [M][H*64]; q_out then takes the scaling of
-// `mode` with factors kh and gate [M][H] (GATED only).  K % 32 == 0; the
-// kernel is persistent, one workgroup per CU (num_cus of the device).
+// `mode` with factors kh and gate [M][H] (GATED only).  K % 32 == 0.
 hipError_t launch_qkv_project(const uint16_t* x, const uint16_t* w, const uint16_t* bias, int64_t M,
                               int K, int H, int mode, const HeadFactors& kh, const uint16_t* gate,
-                              uint16_t* q_out, uint16_t* k_out, uint16_t* v_out, int num_cus,
-                              hipStream_t s);
+                              uint16_t* q_out, uint16_t* k_out, uint16_t* v_out, hipStream_t s);
 
 }  // namespace sdm

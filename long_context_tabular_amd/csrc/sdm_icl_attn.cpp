@@ -1104,7 +1104,7 @@ sdm_icl_status sdm_icl_qkv_project(const void* x, const void* w, const void* bia
   hipError_t e = launch_qkv_project((const uint16_t*)x, (const uint16_t*)w, (const uint16_t*)bias,
                                     (int64_t)batch * rows, in_features, heads, scale_mode, kh,
                                     (const uint16_t*)gate, (uint16_t*)q_out, (uint16_t*)k_out,
-                                    (uint16_t*)v_out, di.cus, (hipStream_t)stream);
+                                    (uint16_t*)v_out, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "qkv_project: launch");
   return SDM_ICL_OK;
 }
