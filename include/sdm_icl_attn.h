@@ -138,7 +138,8 @@ typedef struct {
 sdm_icl_status sdm_icl_attn_fit(const sdm_icl_fit_args* args, sdm_icl_cache* out);
 
 /* Device workspace (bytes) that sdm_icl_attn_query needs for n_query rows:
- * fp32 split partials (m, l and an unnormalised O row per KV split). */
+ * per KV split, (m, l) in fp32 and the split's normalised output row O / l in
+ * fp16. */
 sdm_icl_status sdm_icl_attn_query_workspace_size(sdm_icl_cache cache, int64_t n_query,
                                                  size_t* bytes);
 

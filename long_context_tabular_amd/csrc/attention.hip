@@ -336,7 +336,7 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
         const int64_t slot = ((int64_t)bh * a.q_rows_valid + r) * a.splits + split;
         *reinterpret_cast<float2*>(a.part_ml + slot * 2) = make_float2(-INFINITY, 0.f);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) reinterpret_cast<f32x4*>(a.part_o + slot * 64)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 8; ++i) reinterpret_cast<i32x4*>(a.part_o + slot * 64)[i] = i32x4{0, 0, 0, 0};
       }
     }
     return;
@@ -459,13 +459,17 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
       if (q < q_valid) {
         const int64_t slot = ((int64_t)bh * a.q_rows_valid + q) * a.splits + split;
         if (hf == 0) *reinterpret_cast<float2*>(a.part_ml + slot * 2) = make_float2(ws.m_run[g], l_tot);
+        // the split's normalised output O / l in fp16 (l > 0 whenever the
+        // split holds keys; the combine weighs each split by its l)
+        const float inv_l = l_tot > 0.f ? 1.0f / l_tot : 0.f;
 #pragma unroll
         for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
-            const f32x4 v4 = {ws.o[g][dt][4 * p], ws.o[g][dt][4 * p + 1], ws.o[g][dt][4 * p + 2],
-                              ws.o[g][dt][4 * p + 3]};
-            *reinterpret_cast<f32x4*>(a.part_o + slot * 64 + 32 * dt + 8 * p + 4 * hf) = v4;
+            f16x4 v4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v4[e] = (_Float16)(ws.o[g][dt][4 * p + e] * inv_l);
+            *reinterpret_cast<f16x4*>(a.part_o + slot * 64 + 32 * dt + 8 * p + 4 * hf) = v4;
           }
       }
     } else {
@@ -501,14 +505,15 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 // One wavefront per (b, h, row); splits are taken 64 at a time.  Lane s of
-// a chunk owns split s for the maximum M, the weight w_s = exp2(m_s - M) and
-// the weighted l.  For the head-dim sum, lane 16g + j owns d in [4j, 4j + 4)
+// a chunk owns split s for the maximum M and the weight
+// w_s = exp2(m_s - M) * l_s of its normalised output O_s / l_s (fp16); the
+// row's result is sum_s w_s (O_s / l_s) / sum_s w_s.  For the head-dim sum, lane 16g + j owns d in [4j, 4j + 4)
 // and the splits s = g (mod 4) of the chunk: it issues all of their loads
 // first and then adds them in increasing s; the four partial sums are added
 // in a fixed butterfly order, (g0 + g1) + (g2 + g3).  The order of every sum
 // is fixed, so a row's result does not depend on the launch or on the other
 // rows.
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part_o,
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
                                                       const float* __restrict__ s_v, int B, int H,
                                                       int64_t rows, int splits, int fp8,
@@ -519,25 +524,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int64_t bh = item / rows, r = item - bh * rows;
   const int b = (int)(bh / H), h = (int)(bh - (int64_t)b * H);
   const float* ml = part_ml + item * splits * 2;
-  const float* po = part_o + item * splits * 64;
+  const uint16_t* po = part_o + item * splits * 64;
+  const int g = lane >> 4, j = lane & 15;
+  float l = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY;
   for (int s0 = 0; s0 < splits; s0 += 64)
     if (s0 + lane < splits) m = fmaxf(m, ml[2 * (s0 + lane)]);
   m = wave_max(m);
-  const int g = lane >> 4, j = lane & 15;
-  float l = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int s0 = 0; s0 < splits; s0 += 64) {
     const int sl = s0 + lane;
-    const float wl = sl < splits ? __builtin_amdgcn_exp2f(ml[2 * sl] - m) : 0.f;
-    l += wave_sum(sl < splits ? wl * ml[2 * sl + 1] : 0.f);
+    const float wl = sl < splits ? __builtin_amdgcn_exp2f(ml[2 * sl] - m) * ml[2 * sl + 1] : 0.f;
+    l += wave_sum(wl);
     const int cnt = splits - s0 < 64 ? splits - s0 : 64;
-    const f32x4* pos = reinterpret_cast<const f32x4*>(po + (int64_t)s0 * 64) + j;
-    f32x4 o[16];
+    const f16x4* pos = reinterpret_cast<const f16x4*>(po + (int64_t)s0 * 64) + j;
+    f16x4 o[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int s = g + 4 * i;
-      o[i] = s < cnt ? pos[s * 16] : f32x4{0.f, 0.f, 0.f, 0.f};
+      o[i] = s < cnt ? pos[s * 16] : f16x4{};
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -545,7 +550,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       const float ws = __shfl(wl, s, 64);
       if (s < cnt) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(ws, o[i][e], acc[e]);
+        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(ws, (float)o[i][e], acc[e]);
       }
     }
   }
@@ -592,7 +597,7 @@ hipError_t launch_attention(const AttnArgs& a, int prec, bool split, hipStream_t
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const float* part_o, const float* part_ml, const float* s_v, int B,
+hipError_t launch_combine(const uint16_t* part_o, const float* part_ml, const float* s_v, int B,
                           int H, int64_t rows, int splits, int prec, uint16_t* out,
                           hipStream_t s) {
   const int64_t items = (int64_t)B * H * rows;

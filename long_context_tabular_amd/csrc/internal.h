@@ -28,7 +28,7 @@ struct AttnArgs {
   const void* vt;         // cache V: [B*H][n_alloc/64][64 d][64 keys], keys >= n are 0
   const float* scales;    // device [3][B*H]: s_q, s_k, s_v
   uint16_t* out;          // final mode: fp16 [B][out_rows][H][64]
-  float* part_o;          // split mode: [B*H][q_rows_valid][splits][64]
+  uint16_t* part_o;       // split mode: [B*H][q_rows_valid][splits][64] fp16, O / l of the split
   float* part_ml;         // split mode: [B*H][q_rows_valid][splits][2] = (m in log2 units, l)
   int64_t q_rows_alloc;   // rows per (b,h) of the Q buffer (multiple of kQueryPad)
   int64_t q_rows_valid;   // query rows that exist (context: n; cached query: R)
@@ -91,7 +91,7 @@ hipError_t launch_attention(const AttnArgs& a, int prec, bool split, hipStream_t
                             int grid_splits = 0);
 
 // K5: merge the splits of every (b, h, row) in a fixed order and write fp16 rows.
-hipError_t launch_combine(const float* part_o, const float* part_ml, const float* s_v,
+hipError_t launch_combine(const uint16_t* part_o, const float* part_ml, const float* s_v,
                           int B, int H, int64_t rows, int splits, int prec, uint16_t* out,
                           hipStream_t s);
 

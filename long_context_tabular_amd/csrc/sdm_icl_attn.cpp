@@ -250,7 +250,7 @@ QueryLayout query_layout(const sdm_icl_cache_s* c, int64_t R) {
   size_t off = (size_t)round_up((int64_t)c->B * c->H * L.q_rows_alloc * kHeadDim * eb, 256);
   L.po_off = off;
   if (c->splits > 1) {
-    off += (size_t)round_up((int64_t)c->B * c->H * R * c->splits * kHeadDim * 4, 256);
+    off += (size_t)round_up((int64_t)c->B * c->H * R * c->splits * kHeadDim * 2, 256);
     L.ml_off = off;
     off += (size_t)round_up((int64_t)c->B * c->H * R * c->splits * 2 * 4, 256);
   } else {
@@ -439,7 +439,7 @@ hipError_t streamed_attention(sdm_icl_cache_s* c, AttnArgs at, char* w, const Qu
     for (int kv = 0; kv < 2; ++kv) stage[b][kv] = (unsigned char*)w + L.stage_off + (2 * b + kv) * L.stage_bytes;
   const bool split = c->splits > 1;
   if (split) {
-    at.part_o = (float*)(w + L.po_off);
+    at.part_o = (uint16_t*)(w + L.po_off);
     at.part_ml = (float*)(w + L.ml_off);
   } else {
     at.out = out;
@@ -718,7 +718,7 @@ sdm_icl_status sdm_icl_attn_query(sdm_icl_cache c, const void* q, const void* ga
     return SDM_ICL_OK;
   }
   if (c->splits > 1) {
-    at.part_o = (float*)(w + L.po_off);
+    at.part_o = (uint16_t*)(w + L.po_off);
     at.part_ml = (float*)(w + L.ml_off);
     {
       TimedLaunch tl(SDM_ICL_TIMING_QUERY, s);
