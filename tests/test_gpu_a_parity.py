@@ -115,6 +115,8 @@ CASES = [
     ("ctx128k_fp8", 4096, 4096, 300),
     ("model512k_fp8_log", 3000, 2000, 256),     # NaN tail, partial tiles
     ("cached512k_fp8_gated", 2048, 2048, 129),
+    ("ctx128k_fp8", 128, 100, 40),              # FP8 context of <= 128 rows (one group per wavefront)
+    ("model512k_fp8_log", 320, 129, 1),         # 129 rows: one key in the last tile, one query row
 ]
 
 
