@@ -23,11 +23,17 @@
  *     L32 = fp32(ln(max(n, 1)))   (float32 length arithmetic, clamped log)
  *
  * With FP8 precision ("[FP8 3/4] ...", introduction) Q~, K and V are
- * quantised to OCP e4m3 with per-(batch, head) scales s = amax/448 taken over
- * the valid context rows (for Q, over the *scaled context* queries), codes =
- * e4m3_rne(clamp(fp32(x * (448/amax)), -448, 448)).  Query rows reuse the
- * context's Q scale, so a row's result does not depend on how the queries are
- * split into batches.  Softmax and accumulation are fp32; outputs are fp16.
+ * quantised to OCP e4m3 with per-(batch, head) scales taken over the valid
+ * context rows, codes = e4m3_rne(clamp(fp32(x * inv), -448, 448)).  K and V:
+ * s = amax/448, inv = 448/amax.  Q (from the *scaled context* queries): the
+ * smallest context-derived scale for which the logit of one unit of
+ * sum_d q_code k_code is a power of two, q_unit = 2^E: with
+ * base = fp32(fp32(log2(e)/sqrt(D)) * s_k), E is the smallest integer with
+ * fp32(amax_q * base) <= 448 * 2^E and inv_q = base * 2^-E (E = 0 for an
+ * all-zero Q); the attention kernels apply 2^E exactly as the MFMA's operand
+ * scale.  Query rows reuse the context's Q scale, so a row's result does not
+ * depend on how the queries are split into batches.  Softmax and
+ * accumulation are fp32; outputs are fp16.
  *
  * Conventions (all entry points)
  * ------------------------------
@@ -168,8 +174,8 @@ sdm_icl_status sdm_icl_attn_cache_lengths(sdm_icl_cache cache, int64_t* host_len
 /* Copy the cached operands to host memory (parity checks, persistence).
  * host_k / host_v: [B, H, n, D] elements with n = n_valid (rows n_b..n-1 of a
  * shorter batch element are 0), 1 byte (e4m3 code) in FP8 mode or
- * 2 bytes (fp16) in FP16 mode; host_scales: float32 [3, B, H] = s_q, s_k, s_v
- * (all 1 in FP16 mode).  Any of the three may be NULL.  Synchronises `stream`. */
+ * 2 bytes (fp16) in FP16 mode; host_scales: float32 [3, B, H] = q_unit, s_k,
+ * s_v (all 1 in FP16 mode).  Any of the three may be NULL.  Synchronises `stream`. */
 sdm_icl_status sdm_icl_attn_cache_export(sdm_icl_cache cache, void* host_k, void* host_v,
                                          float* host_scales, void* stream);
 
@@ -184,18 +190,19 @@ typedef struct {
   const void* host_k;         /* host [B, H, n, D], n = max n_b, as cache_export writes it:
                                  e4m3 codes (1 byte) or fp16; rows >= n_b are ignored */
   const void* host_v;         /* host [B, H, n, D], same element type */
-  const float* host_scales;   /* host float32 [3, B, H]: s_q, s_k, s_v (all 1 for FP16) */
+  const float* host_scales;   /* host float32 [3, B, H]: q_unit, s_k, s_v (all 1 for FP16) */
   void* stream;               /* hipStream_t */
 } sdm_icl_import_args;
 
 /* Rebuild a cache from what cache_export wrote (persistence, migration to
  * another device or process; the pages' FP8 caches are migrated and
  * preserved through chunking, "[FP8 3/4] ...", walkthrough).  FP8 codes and
- * scales are taken as they are; the inverse scales the query quantiser needs
- * are recovered exactly from s = fp32(amax/448) (the amax is an fp16 value),
- * so queries on the imported cache reproduce those on the exported one bit
- * for bit.  Scales that are not of that form are SDM_ICL_E_INVALID, as are
- * e4m3 NaN codes (0x7F, 0xFF).  Allocates the cache on args->stream and
+ * scales are taken as they are; the inverse scales are recovered exactly, for
+ * K and V from s = fp32(amax/448) (the amax is an fp16 value), for Q from
+ * q_unit and s_k, so queries on the imported cache reproduce those on the
+ * exported one bit for bit.  K/V scales not of that form and a q_unit that
+ * is not a normal power of two are SDM_ICL_E_INVALID, as are e4m3 NaN codes
+ * (0x7F, 0xFF).  Allocates the cache on args->stream and
  * synchronises that stream before it returns. */
 sdm_icl_status sdm_icl_attn_cache_import(const sdm_icl_import_args* args, sdm_icl_cache* out);
 
@@ -229,7 +236,8 @@ sdm_icl_status sdm_icl_attn_release(sdm_icl_cache cache);
  * head_coef: host float32 [H] unless NONE.  out: device, head-major
  * [B, H, rows, D]: fp16 when q_inv_scale is NULL, else e4m3 codes (1 byte)
  * of the scaled rows quantised with the device float32 inverse scales
- * q_inv_scale [B, H] (448 / amax). */
+ * q_inv_scale [B, H] (for a cache's queries, the Q inverse scales its fit
+ * derived). */
 sdm_icl_status sdm_icl_log_scale(const void* q, const void* gate, int32_t batch, int64_t rows,
                                  int32_t heads, int32_t head_dim, int64_t key_length,
                                  const float* head_coef, int32_t scale_mode,

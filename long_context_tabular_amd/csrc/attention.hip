@@ -85,12 +85,14 @@ struct Ops<kPrecFp8> {
   __device__ static QFrag load_q(const unsigned char* rowp, int hf) {
     return *reinterpret_cast<const i32x8*>(rowp + 32 * hf);
   }
-  __device__ static f32x16 qk(const unsigned char* krow, int hf, const QFrag& q) {
+  // c + 2^E * (K rows . Q): the Q operand carries the E8M0 scale q_unit8 =
+  // 127 + E, so the result is the logit in log2 units (plus c)
+  __device__ static f32x16 qk(const unsigned char* krow, int hf, const QFrag& q, const f32x16& c,
+                              int q_unit8) {
     const i32x4 a0 = *reinterpret_cast<const i32x4*>(krow + 32 * hf);
     const i32x4 a1 = *reinterpret_cast<const i32x4*>(krow + 32 * hf + 16);
     const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-    const f32x16 z = {};
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, q, z, 0, 0, 0, 0, 0, 0);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, q, c, 0, 0, 0, 127, 0, q_unit8);
   }
 };
 
@@ -105,8 +107,8 @@ struct Ops<kPrecFp16> {
     for (int t = 0; t < 4; ++t) f.v[t] = *reinterpret_cast<const f16x8*>(rowp + 32 * t + 16 * hf);
     return f;
   }
-  __device__ static f32x16 qk(const unsigned char* krow, int hf, const QFrag& q) {
-    f32x16 acc = {};
+  __device__ static f32x16 qk(const unsigned char* krow, int hf, const QFrag& q, const f32x16& c, int) {
+    f32x16 acc = c;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const f16x8 a = *reinterpret_cast<const f16x8*>(krow + 32 * t + 16 * hf);
@@ -143,16 +145,8 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
   return fmaxf(lo, hi);
 }
 
-// P = fp16(exp2(s * c - m)) for the lane's 16 scores of one 32-key chunk;
-// returns the fp32 sum of the rounded P (v_dot2 of each packed fp16 pair
-// with (1, 1)).
-__device__ __forceinline__ float exp_chunk(const f32x16& s, float c_scale, float neg_m,
-                                           f16x8 (&p16)[2]) {
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      p16[ks][e] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * ks + e], c_scale, neg_m));
+// fp32 sum of 16 fp16 P values (v_dot2 of each packed pair with (1, 1)).
+__device__ __forceinline__ float sum_p(const f16x8 (&p16)[2]) {
   const h16x2 ones = {(__fp16)1.0f, (__fp16)1.0f};
   float lsum = 0.f;
 #pragma unroll
@@ -170,11 +164,44 @@ __device__ __forceinline__ float exp_chunk(const f32x16& s, float c_scale, float
   return lsum;
 }
 
-// Scores of one 32-key chunk with keys >= n set to -inf (MASK only).
+// P = fp16(exp2(s * c - m)) for the lane's 16 scores of one 32-key chunk;
+// returns the fp32 sum of the rounded P (v_dot2 of each packed fp16 pair
+// with (1, 1)).
+__device__ __forceinline__ float exp_chunk(const f32x16& s, float c_scale, float neg_m,
+                                           f16x8 (&p16)[2]) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      p16[ks][e] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * ks + e], c_scale, neg_m));
+  return sum_p(p16);
+}
+
+// How a raw score becomes a logit in log2 units: FP16 multiplies by c
+// (log2(e)/sqrt(D)); FP8 gets the whole factor from the MFMA's operand scale
+// (q_unit8, an E8M0 exponent) and has c = 1.
+struct Logit {
+  float c;
+  int q_unit8;
+};
+
+// P = fp16(exp2(x)) for logits x already shifted by the reference (FP8:
+// the MFMA accumulates onto -m); same rounding of P and l as exp_chunk.
+__device__ __forceinline__ float exp_chunk_shifted(const f32x16& x, f16x8 (&p16)[2]) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p16[ks][e] = (_Float16)__builtin_amdgcn_exp2f(x[8 * ks + e]);
+  return sum_p(p16);
+}
+
+// Scores of one 32-key chunk, starting from the accumulator value init, with
+// keys >= n set to -inf (MASK only).
 template <int PREC, bool MASK>
 __device__ __forceinline__ f32x16 chunk_scores(const unsigned char* kb, int c, int col, int hf,
-                                               const typename Ops<PREC>::QFrag& q, int rem) {
-  f32x16 sc = Ops<PREC>::qk(kb + (32 * c + col) * Ops<PREC>::KROW, hf, q);
+                                               const typename Ops<PREC>::QFrag& q, int rem, Logit lg,
+                                               const f32x16& init = f32x16{}) {
+  f32x16 sc = Ops<PREC>::qk(kb + (32 * c + col) * Ops<PREC>::KROW, hf, q, init, lg.q_unit8);
   if constexpr (MASK) {
     const int lim = rem - 8 * hf;  // key offset in the tile = 32c + 16(r/8) + 8hf + r%8
 #pragma unroll
@@ -192,15 +219,16 @@ __device__ __forceinline__ f32x16 chunk_scores(const unsigned char* kb, int c, i
 // the scores instead of keeping them.
 template <int PREC, int QG, bool FIRST, bool MASK>
 __device__ __forceinline__ void attend_tile(WaveState<PREC, QG>& w, const unsigned char* kb,
-                                            const unsigned char* vb, float c_scale, int col,
+                                            const unsigned char* vb, Logit lg, int col,
                                             int hf, int rem) {
+  const float c_scale = lg.c;
   f16x8 p16[QG][2][2];
   if constexpr (FIRST) {
 #pragma unroll
     for (int g = 0; g < QG; ++g) {
       f32x16 s[2];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) s[c] = chunk_scores<PREC, MASK>(kb, c, col, hf, w.qf[g], rem);
+      for (int c = 0; c < 2; ++c) s[c] = chunk_scores<PREC, MASK>(kb, c, col, hf, w.qf[g], rem, lg);
       w.m_run[g] = tile_max(s) * c_scale;
       w.l_run[g] = exp_chunk(s[0], c_scale, -w.m_run[g], p16[g][0]) +
                    exp_chunk(s[1], c_scale, -w.m_run[g], p16[g][1]);
@@ -214,10 +242,20 @@ __device__ __forceinline__ void attend_tile(WaveState<PREC, QG>& w, const unsign
 #pragma unroll
     for (int g = 0; g < QG; ++g) {
       lt[g] = 0.f;
+      if constexpr (PREC == kPrecFp8) {
+        // the MFMA starts from -m, so it returns the logit minus the
+        // reference and P needs no per-score arithmetic before exp2
+        const f32x16 neg_m = -w.m_run[g];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const f32x16 sc = chunk_scores<PREC, MASK>(kb, c, col, hf, w.qf[g], rem);
-        lt[g] += exp_chunk(sc, c_scale, -w.m_run[g], p16[g][c]);
+        for (int c = 0; c < 2; ++c)
+          lt[g] += exp_chunk_shifted(chunk_scores<PREC, MASK>(kb, c, col, hf, w.qf[g], rem, lg, neg_m),
+                                     p16[g][c]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const f32x16 sc = chunk_scores<PREC, MASK>(kb, c, col, hf, w.qf[g], rem, lg);
+          lt[g] += exp_chunk(sc, c_scale, -w.m_run[g], p16[g][c]);
+        }
       }
       ok = ok && (lt[g] <= kMaxLaneSum);  // false for inf
     }
@@ -234,7 +272,7 @@ __device__ __forceinline__ void attend_tile(WaveState<PREC, QG>& w, const unsign
         if (__builtin_amdgcn_ballot_w64(over) == 0) continue;
         f32x16 s[2];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) s[c] = chunk_scores<PREC, MASK>(kb, c, col, hf, w.qf[g], rem);
+        for (int c = 0; c < 2; ++c) s[c] = chunk_scores<PREC, MASK>(kb, c, col, hf, w.qf[g], rem, lg);
         const float mt = tile_max(s) * c_scale;
         const float mnew = over ? fmaxf(w.m_run[g], mt) : w.m_run[g];
         const float alpha = __builtin_amdgcn_exp2f(w.m_run[g] - mnew);
@@ -298,10 +336,13 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
     return;
   }
 
-  float c_scale = a.tau_log2e;  // logit (log2 units) = raw dot * c_scale
+  // logit (log2 units) = raw dot * c_scale (FP16); FP8: the Q slot of the
+  // scales holds q_unit = 2^E, whose exponent field is the E8M0 operand scale
+  // that makes the MFMA return the logit itself
+  Logit c_scale = {a.tau_log2e, 127};
   float sv = 1.0f;
   if constexpr (PREC == kPrecFp8) {
-    c_scale *= a.scales[bh] * a.scales[a.bh_count + bh];
+    c_scale = {1.0f, (int)((__float_as_uint(a.scales[bh]) >> 23) & 0xFF)};
     sv = a.scales[2 * a.bh_count + bh];
   }
 

@@ -12,6 +12,9 @@ constexpr int kHeadDim = 64;       // D: the only head width the kernels are bui
 constexpr int kKeyTile = 64;       // keys per K/V tile (one LDS stage)
 constexpr int kQueryPad = 256;     // Q operand buffers are padded to this many rows
 constexpr int kMaxHeads = 128;
+// fp32 of log2(e) / sqrt(D): the base-2 logit factor of scaled dot-product
+// attention at D = 64
+constexpr float kLog2eTau = (float)(1.4426950408889634 / 8.0);
 
 constexpr int kScaleNone = 0, kScaleLog = 1, kScaleGated = 2;
 constexpr int kPrecFp16 = 0, kPrecFp8 = 1;

@@ -155,13 +155,36 @@ __global__ void fill_f32_kernel(float* p, int64_t count, float value) {
 
 // s = fp32(a / 448), inv = fp32(448 / a); a = 0 gives 1 and 1.  Division is
 // the correctly rounded IEEE float32 division.
+// Scales from the amaxes [3][B*H] (Q, K, V).  K and V: s = a / 448,
+// inv = 448 / a (a = 0 -> 1).  Q: the smallest scale for which the logit of
+// one unit of sum_d q_code k_code is a power of two: with
+// base = fp32(log2(e)/sqrt(D)) * s_k, E is the smallest integer with
+// fp32(a_q * base) <= 448 * 2^E (E = 0 for a = 0); the Q slot holds
+// q_unit = 2^E and inv_q = base * 2^-E, so the attention kernels apply the
+// whole logit factor through the MFMA's power-of-two operand scale.
 __global__ void scales_kernel(const uint32_t* __restrict__ amax_bits, int count,
                               float* __restrict__ scales, float* __restrict__ inv) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= count) return;
+  const int bh_count = count / 3;
   const float a = __uint_as_float(amax_bits[i]);
-  scales[i] = a == 0.f ? 1.f : a / 448.0f;
-  inv[i] = a == 0.f ? 1.f : 448.0f / a;
+  if (i >= bh_count) {
+    scales[i] = a == 0.f ? 1.f : a / 448.0f;
+    inv[i] = a == 0.f ? 1.f : 448.0f / a;
+    return;
+  }
+  const float ak = __uint_as_float(amax_bits[bh_count + i]);
+  const float s_k = ak == 0.f ? 1.f : ak / 448.0f;
+  const float base = kLog2eTau * s_k;
+  int e = 0;
+  if (a != 0.f) {
+    const float v = a * base;
+    e = (int)ceilf(log2f(v / 448.0f));
+    while (ldexpf(448.0f, e) < v) ++e;
+    while (ldexpf(448.0f, e - 1) >= v) --e;
+  }
+  scales[i] = ldexpf(1.0f, e);
+  inv[i] = ldexpf(base, -e);
 }
 
 // ---------------------------------------------------------------- K2

@@ -275,7 +275,7 @@ AttnArgs attn_args(const sdm_icl_cache_s* c) {
   a.n_alloc = c->n_alloc;
   a.heads = c->H;
   a.bh_count = c->B * c->H;
-  a.tau_log2e = (float)(1.4426950408889634 / std::sqrt((double)kHeadDim));
+  a.tau_log2e = kLog2eTau;
   return a;
 }
 
@@ -406,6 +406,12 @@ float f16_bits_to_f32(uint16_t h) {
 // the fp16 amax: a is the one fp16 value whose quotient by 448 rounds to s
 // (distinct fp16 values differ by at least 2^-11 relative, so their fp32
 // quotients differ).  s = 1 stands for a = 0 or a = 448, both giving inv = 1.
+uint32_t float_bits(float x) {
+  uint32_t b;
+  std::memcpy(&b, &x, sizeof b);
+  return b;
+}
+
 bool inverse_from_scale(float s, float* inv) {
   if (!(s > 0.f) || !std::isfinite(s)) return false;
   if (s == 1.f) { *inv = 1.f; return true; }
@@ -839,16 +845,25 @@ sdm_icl_status sdm_icl_attn_cache_import(const sdm_icl_import_args* a, sdm_icl_c
   }
   const bool fp8 = a->precision == SDM_ICL_PREC_FP8_E4M3;
   const int64_t eb = fp8 ? 1 : 2, BH = (int64_t)B * H;
-  // scales and the inverse scales they imply
+  // scales and the inverse scales they imply: K and V first, then the Q
+  // slot, whose inverse follows from s_k and q_unit = 2^E
   std::vector<float> sc(6 * BH);
-  for (int64_t i = 0; i < 3 * BH; ++i) {
+  for (int64_t i = 3 * BH - 1; i >= 0; --i) {
     const float sv = a->host_scales[i];
     float inv;
     if (!fp8) {
       if (sv != 1.f) return fail(SDM_ICL_E_INVALID, "import: FP16 caches have unit scales");
       inv = 1.f;
-    } else if (!inverse_from_scale(sv, &inv)) {
-      return fail(SDM_ICL_E_INVALID, "import: scale %lld (%g) is not fp32(amax/448) of an fp16 amax", (long long)i, (double)sv);
+    } else if (i >= BH) {
+      if (!inverse_from_scale(sv, &inv))
+        return fail(SDM_ICL_E_INVALID, "import: scale %lld (%g) is not fp32(amax/448) of an fp16 amax",
+                    (long long)i, (double)sv);
+    } else {
+      const uint32_t bits = float_bits(sv);
+      const int ex = (int)((bits >> 23) & 0xFF);
+      if ((bits & 0x807FFFFFu) != 0 || ex == 0 || ex == 0xFF)
+        return fail(SDM_ICL_E_INVALID, "import: Q scale %lld (%g) is not a power of two", (long long)i, (double)sv);
+      inv = std::ldexp(kLog2eTau * sc[BH + i], -(ex - 127));
     }
     sc[i] = sv;
     sc[3 * BH + i] = inv;

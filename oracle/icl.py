@@ -23,10 +23,19 @@ reason in the design notes of the repository):
 * LogScale: ``q~ = fp16(q * k_h)``.  GatedLogScale:
   ``q~ = fp16(fp16(q * k_h) * fp16(1 + fp16(tanh g)))`` with one gate value
   per row and head.
-* FP8 scales per (batch, head) from the amax over valid rows: ``s = fp32(a /
-  448)``, ``inv = fp32(448 / a)`` (a = 0 gives s = inv = 1); codes are
-  ``e4m3(clamp(fp32(x * inv), +-448))``.  The Q scale comes from the *scaled*
-  context queries; query rows reuse it (and saturate above it).
+* FP8 scales per (batch, head) from the amax over valid rows: for K and V
+  ``s = fp32(a / 448)``, ``inv = fp32(448 / a)`` (a = 0 gives s = inv = 1);
+  codes are ``e4m3(clamp(fp32(x * inv), +-448))``.  The Q scale comes from
+  the *scaled* context queries (query rows reuse it and saturate above it)
+  and is the smallest one for which the logit of one unit of
+  ``sum_d q_code k_code`` is a power of two: with ``base = fp32(fp32(log2(e)
+  / sqrt(D)) * s_k)``, ``inv_q = base * 2^-E`` for the smallest integer E
+  with ``fp32(a_q * base) <= 448 * 2^E``, and the logit in log2 units is
+  ``2^E * sum_d q_code k_code`` exactly (``q_unit = 2^E`` is kept where the
+  Q scale would be; the dequantised Q scale is ``2^E ln 2 / (tau s_k)``).
+  The pages only ask for a context-derived Q scale; e4m3 is a floating-point
+  format, so the factor in [1, 2) this costs shifts Q's range by less than
+  one binade and leaves its relative precision unchanged.
 * masked context rows (index >= n) are not keys, not part of n and not part
   of any amax; their outputs are zero.
 * per-batch lengths (the pages' fused path covers one shared int and falls
@@ -129,6 +138,31 @@ def fp8_scale(amax) -> tuple:
     if a == 0:
         return np.float32(1.0), np.float32(1.0)
     return np.float32(a / np.float32(E4M3_MAX)), np.float32(np.float32(E4M3_MAX) / a)
+
+
+def log2e_tau_f32(head_dim: int = 64) -> np.float32:
+    """float32 of log2(e) / sqrt(D): the base-2 logit factor of SDPA."""
+    return np.float32(1.4426950408889634 / math.sqrt(head_dim))
+
+
+def fp8_query_scale(amax_q, s_k, head_dim: int = 64) -> tuple:
+    """(q_unit = 2^E, inv_q) in float32 for one (batch, head) of the Q operand.
+
+    ``base = fp32(fp32(log2 e / sqrt D) * s_k)``; E is the smallest integer
+    with ``fp32(amax_q * base) <= 448 * 2^E`` (E = 0 for an all-zero Q), and
+    ``inv_q = base * 2^-E``, so the amax quantises to at most 448 and the
+    logit of one unit of sum_d q_code k_code is exactly 2^E in log2 units."""
+    base = np.float32(log2e_tau_f32(head_dim) * np.float32(s_k))
+    a = np.float32(amax_q)
+    e = 0
+    if a != 0:
+        v = float(np.float32(a * base))
+        e = math.ceil(math.log2(v / E4M3_MAX))
+        while math.ldexp(E4M3_MAX, e) < v:
+            e += 1
+        while math.ldexp(E4M3_MAX, e - 1) >= v:
+            e -= 1
+    return np.float32(math.ldexp(1.0, e)), np.float32(math.ldexp(float(base), -e))
 
 
 def amax_rows(x: np.ndarray) -> np.ndarray:
@@ -259,10 +293,15 @@ class OracleCache:
         return self.v16[b][:, h, :].astype(np.float64)
 
     def qhat(self, qt: np.ndarray, b: int, h: int) -> np.ndarray:
-        """Operand used for scaled query rows qt ``[m, H, D]`` (fp16) of head h."""
+        """Operand used for scaled query rows qt ``[m, H, D]`` (fp16) of head h.
+
+        FP8: the codes times the dequantised Q scale ``q_unit ln 2 / (tau
+        s_k)``, so that tau * qhat . khat = q_unit * ln 2 * sum of code
+        products, i.e. 2^E * sum in log2 units."""
         x = qt[:, h, :]
         if self.precision == PREC_FP8_E4M3:
-            return quantize(x, self.inv[0, b, h]) * np.float64(self.scales[0, b, h])
+            s_q = np.float64(self.scales[0, b, h]) * math.log(2.0) / (self.tau * np.float64(self.scales[1, b, h]))
+            return quantize(x, self.inv[0, b, h]) * s_q
         return x.astype(np.float64)
 
 
@@ -309,6 +348,9 @@ def fit(q: np.ndarray, k: np.ndarray, v: np.ndarray, n, scale_mode: int,
                 a = amax_rows(x)
                 for h in range(H):
                     scales[t, b, h], inv[t, b, h] = fp8_scale(a[h])
+            a = amax_rows(qt)
+            for h in range(H):
+                scales[0, b, h], inv[0, b, h] = fp8_query_scale(a[h], scales[1, b, h], D)
             kc = np.empty((H, nb, D), dtype=np.uint8)
             vc = np.empty((H, nb, D), dtype=np.uint8)
             for h in range(H):

@@ -372,11 +372,16 @@ def test_fused_projection_scaling_is_the_separate_pass():
     assert not np.array_equal(qs, q)
 
 
-def test_fp8_is_lossless_on_grid_inputs():
-    """I10: when Q~, K, V already lie on the e4m3 grid with amax = 448 s, FP8
-    quantisation changes nothing and the FP8 result equals the FP16 one.  Each
-    tensor and head gets its own power-of-two scale so that a mixed-up scale
-    (s_k used for V, say) changes the result."""
+def test_fp8_grid_inputs_and_the_query_scale_rule():
+    """I10, restated for the Q scale rule.  K and V on the e4m3 grid with
+    amax = 448 s (each tensor and head its own power-of-two scale) quantise
+    losslessly, so a mixed-up K/V scale changes the result.  The Q scale:
+    q_unit is a power of two, the Q amax lands in (224, 448] once scaled (E is
+    the smallest exponent that keeps it in range), and inv_q * q_unit is the
+    rule's base fp32(fp32(log2 e / 8) * s_k).  The output equals a softmax in
+    base 2 over 2^E * (sum of code products), computed here straight from the
+    codes (so the ln 2 / tau bookkeeping of the dequantised operands is
+    checked by a different route)."""
     rng = np.random.default_rng(3)
     B, N, H, D = 1, 96, 2, 64
     grid = numerics.E4M3_VALUES[np.isfinite(numerics.E4M3_VALUES)]
@@ -392,13 +397,29 @@ def test_fp8_is_lossless_on_grid_inputs():
         return t.astype(np.float16)
     q, k, v = draw("q"), draw("k"), draw("v")
     c8 = icl.fit(q, k, v, N, icl.SCALE_NONE, icl.PREC_FP8_E4M3)
-    c16 = icl.fit(q, k, v, N, icl.SCALE_NONE, icl.PREC_FP16)
-    for t, name in enumerate("qkv"):
+    for t, name in ((1, "k"), (2, "v")):
         np.testing.assert_array_equal(c8.scales[t, 0], np.float32(scales[name]))
+    np.testing.assert_array_equal(numerics.E4M3_VALUES[c8.k_codes[0]] * np.array(scales["k"])[:, None, None],
+                                  k[0].transpose(1, 0, 2).astype(np.float64))
+    np.testing.assert_array_equal(numerics.E4M3_VALUES[c8.v_codes[0]] * np.array(scales["v"])[:, None, None],
+                                  v[0].transpose(1, 0, 2).astype(np.float64))
+    base_const = np.float32(1.4426950408889634 / 8)
     rows = np.arange(N)
-    ref = icl.context_outputs(c16, q, None, rows)
-    np.testing.assert_allclose(icl.context_outputs(c8, q, None, rows), ref,
-                               rtol=0, atol=1e-15 * np.abs(ref).max())
+    got = icl.context_outputs(c8, q, None, rows)
+    for h in range(H):
+        qu, inv = c8.scales[0, 0, h], c8.inv[0, 0, h]
+        mant, ex = np.frexp(np.float64(qu))
+        assert mant == 0.5                                            # a power of two
+        base = np.float32(base_const * np.float32(scales["k"][h]))
+        assert np.float64(inv) * np.float64(qu) == np.float64(base)
+        top = np.float32(np.float32(448 * scales["q"][h]) * inv)      # the amax element, scaled
+        assert 224 < top <= 448
+        qc = numerics.e4m3_round(np.clip(q[0, :, h].astype(np.float32) * inv, -448, 448).astype(np.float32))
+        kc = numerics.E4M3_VALUES[c8.k_codes[0, h]]
+        logit2 = np.float64(qu) * (qc.astype(np.float64) @ kc.T)       # log2 units
+        w = np.exp2(logit2 - logit2.max(axis=1, keepdims=True))
+        want = (w @ v[0, :, h].astype(np.float64)) / w.sum(axis=1, keepdims=True)
+        np.testing.assert_allclose(got[:, h], want, rtol=0, atol=1e-12 * np.abs(want).max())
 
 
 def test_query_rows_use_context_q_scale():
@@ -408,7 +429,8 @@ def test_query_rows_use_context_q_scale():
     qt = icl.scale_queries(x.q_ctx[0], icl.SCALE_GATED_LOG, c.k_h, x.gate_ctx[0])
     for h in range(x.workload.heads):
         a = np.max(np.abs(qt[:, h].astype(np.float64)))
-        assert c.scales[0, 0, h] == icl.fp8_scale(a)[0]
+        qu, inv = icl.fp8_query_scale(a, c.scales[1, 0, h])
+        assert c.scales[0, 0, h] == qu and c.inv[0, 0, h] == inv
     # splitting queries into batches cannot change any row
     full = icl.attend(c, x.q_query[0], x.gate_query[0], heads=[1])
     half = np.concatenate([icl.attend(c, x.q_query[0, :16], x.gate_query[0, :16], heads=[1]),
