@@ -286,3 +286,38 @@ def test_reference_moves_when_later_tiles_dominate(prec):
     e_q = norm_err(full[0].astype(np.float64), icl.attend(ref, qq[0], None))
     say(f"  context err {e_c:.3e} query err {e_q:.3e}")
     assert e_c <= TOL[prec] and e_q <= TOL[prec]
+
+
+def test_fp8_query_scale_edges():
+    """The power-of-two Q unit at its edges: an all-zero Q (E = 0; every key
+    equally weighted, so each row returns the mean of the dequantised V) and
+    large-magnitude queries against tiny keys (E far from 0), each against
+    the oracle."""
+    torch = _torch()
+    rng = np.random.default_rng(71)
+    N, H = 300, 2
+    k = (rng.standard_normal((1, N, H, 64)) / 8).astype(np.float16)
+    v = (rng.standard_normal((1, N, H, 64)) / 8).astype(np.float16)
+    cases = {
+        "zero q": (np.zeros((1, N, H, 64), dtype=np.float16), k),
+        "large q, tiny k": ((rng.standard_normal((1, N, H, 64)) * 8000).clip(-65000, 65000).astype(np.float16),
+                            (k.astype(np.float32) * 1e-3).astype(np.float16)),
+    }
+    for name, (q, kk) in cases.items():
+        say("q scale edge:", name)
+        out = torch.empty((1, N, H, 64), dtype=torch.float16, device="cuda")
+        c = B.sdm_icl_attn_fit(to_dev(q), to_dev(kk), to_dev(v), N, precision=B.SDM_ICL_PREC_FP8_E4M3, out_ctx=out)
+        _, _, sc = B.sdm_icl_attn_cache_export(c)
+        c.release()
+        ref = icl.fit(q, kk, v, N, icl.SCALE_NONE, icl.PREC_FP8_E4M3)
+        np.testing.assert_array_equal(sc, ref.scales)
+        rows = np.arange(N)
+        want = icl.context_outputs(ref, q, None, rows)
+        got = out.cpu().numpy()[0].astype(np.float64)
+        err = norm_err(got, want)
+        say(f"  normalised error {err:.2e}, q_unit {sc[0, 0, 0]!r}")
+        assert err <= TOL[B.SDM_ICL_PREC_FP8_E4M3]
+        if name == "zero q":
+            assert sc[0, 0, 0] == 1.0
+            mean_v = np.stack([ref.vhat(0, h).mean(axis=0) for h in range(H)])
+            np.testing.assert_allclose(got, np.broadcast_to(mean_v, got.shape), rtol=0, atol=2e-3 * np.abs(mean_v).max())
