@@ -3,9 +3,10 @@
 //   K3  context self-attention: every valid context row attends to all n
 //       context keys, no causal mask; rows >= n are written as zeros.
 //   K4  cached query attention: the same tile loop over one KV split of the
-//       resident cache, writing (m, l, O) partials.
-//   K5  combine: one wavefront per (b, h, row), lane = head-dim element,
-//       merges the splits in a fixed order.
+//       resident cache, writing (m, l) and the split's normalised output
+//       O / l (fp16) as partials.
+//   K5  combine: one wavefront per (b, h, row) merges the splits in a fixed
+//       order.
 //
 // Semantics: scaled dot-product attention of the (scaled, optionally
 // quantised) queries over the cached keys/values, as in "[FP8 3/4] Integrate
@@ -19,11 +20,15 @@
 //   * 64-key tiles of K and of V are fetched as separate loads into registers
 //     two tiles ahead, and written into separate double-buffered LDS stages
 //     (K row-major, V transposed and widened to fp16), one barrier per tile.
-//   * S^T = K Q^T with v_mfma_f32_32x32x64_f8f6f4 (FP8) or 32x32x16_f16.
-//     K rows are fed in a permuted order so that each lane ends up holding,
-//     for its own query, exactly the 8-key groups that the PV MFMA wants in
-//     its B operand: P never leaves registers.
-//   * Online softmax in base 2 (the scale is folded into one FMA per score).
+//   * S^T = K Q^T with v_mfma_scale_f32_32x32x64_f8f6f4 (FP8) or
+//     32x32x16_f16.  K rows are fed in a permuted order so that each lane
+//     ends up holding, for its own query, exactly the 8-key groups that the
+//     PV MFMA wants in its B operand: P never leaves registers.
+//   * Online softmax in base 2.  FP8: the logit factor is a power of two
+//     (the cache's q_unit = 2^E) that the MFMA applies as its E8M0 operand
+//     scale, and after the first tile the MFMA accumulates onto -m, so it
+//     returns the shifted logit and P = exp2 of it.  FP16: the scale and the
+//     reference are folded into one FMA per score.
 //     The first tile of a wave's KV range sets each row's reference maximum;
 //     later tiles compute P against it with no per-tile max at all, and a row
 //     moves its reference (rescaling O and l) only when the 32 rounded P one
@@ -336,13 +341,13 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
     return;
   }
 
-  // logit (log2 units) = raw dot * c_scale (FP16); FP8: the Q slot of the
+  // logit (log2 units) = raw dot * lg.c (FP16); FP8: the Q slot of the
   // scales holds q_unit = 2^E, whose exponent field is the E8M0 operand scale
   // that makes the MFMA return the logit itself
-  Logit c_scale = {a.tau_log2e, 127};
+  Logit lg = {a.tau_log2e, 127};
   float sv = 1.0f;
   if constexpr (PREC == kPrecFp8) {
-    c_scale = {1.0f, (int)((__float_as_uint(a.scales[bh]) >> 23) & 0xFF)};
+    lg = {1.0f, (int)((__float_as_uint(a.scales[bh]) >> 23) & 0xFF)};
     sv = a.scales[2 * a.bh_count + bh];
   }
 
@@ -467,26 +472,26 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
   const int64_t t_full = (t1 * 64 > n) ? t1 - 1 : t1;
   const int rem_last = (int)(n - (t1 - 1) * 64);
   if (t0 < t_full)
-    attend_tile<PREC, QG, true, false>(ws, kbuf[0], vbuf[0], c_scale, col, hf, 64);
+    attend_tile<PREC, QG, true, false>(ws, kbuf[0], vbuf[0], lg, col, hf, 64);
   else
-    attend_tile<PREC, QG, true, true>(ws, kbuf[0], vbuf[0], c_scale, col, hf, rem_last);
+    attend_tile<PREC, QG, true, true>(ws, kbuf[0], vbuf[0], lg, col, hf, rem_last);
   advance(t0, sa);  // for a one-tile range this stages an unused copy of the last tile
   // tile t0+1+2i takes its successor from sb, tile t0+2+2i from sa
   int64_t t = t0 + 1;
   for (; t + 1 < t_full; t += 2) {
-    attend_tile<PREC, QG, false, false>(ws, kbuf[1], vbuf[1], c_scale, col, hf, 64);
+    attend_tile<PREC, QG, false, false>(ws, kbuf[1], vbuf[1], lg, col, hf, 64);
     advance(t, sb);
-    attend_tile<PREC, QG, false, false>(ws, kbuf[0], vbuf[0], c_scale, col, hf, 64);
+    attend_tile<PREC, QG, false, false>(ws, kbuf[0], vbuf[0], lg, col, hf, 64);
     advance(t + 1, sa);
   }
   if (t < t_full) {
-    attend_tile<PREC, QG, false, false>(ws, kbuf[1], vbuf[1], c_scale, col, hf, 64);
+    attend_tile<PREC, QG, false, false>(ws, kbuf[1], vbuf[1], lg, col, hf, 64);
     advance(t, sb);
     ++t;
   }
   if (t_full > t0 && t_full < t1) {
     const int cur = (int)((t_full - t0) & 1);
-    attend_tile<PREC, QG, false, true>(ws, kbuf[cur], vbuf[cur], c_scale, col, hf, rem_last);
+    attend_tile<PREC, QG, false, true>(ws, kbuf[cur], vbuf[cur], lg, col, hf, rem_last);
   }
 
   // ---- epilogue
