@@ -137,6 +137,7 @@ struct WaveState {
   typename Ops<PREC>::QFrag qf[QG];
   float m_run[QG], l_run[QG];
   f32x16 o[QG][2];
+  f32x16 neg_m[QG];  // FP8: -m_run splatted, the QK MFMA's accumulator input
 };
 
 __device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
@@ -235,6 +236,7 @@ __device__ __forceinline__ void attend_tile(WaveState<PREC, QG>& w, const unsign
 #pragma unroll
       for (int c = 0; c < 2; ++c) s[c] = chunk_scores<PREC, MASK>(kb, c, col, hf, w.qf[g], rem, lg);
       w.m_run[g] = tile_max(s) * c_scale;
+      if constexpr (PREC == kPrecFp8) w.neg_m[g] = -w.m_run[g];
       w.l_run[g] = exp_chunk(s[0], c_scale, -w.m_run[g], p16[g][0]) +
                    exp_chunk(s[1], c_scale, -w.m_run[g], p16[g][1]);
     }
@@ -250,10 +252,9 @@ __device__ __forceinline__ void attend_tile(WaveState<PREC, QG>& w, const unsign
       if constexpr (PREC == kPrecFp8) {
         // the MFMA starts from -m, so it returns the logit minus the
         // reference and P needs no per-score arithmetic before exp2
-        const f32x16 neg_m = -w.m_run[g];
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-          lt[g] += exp_chunk_shifted(chunk_scores<PREC, MASK>(kb, c, col, hf, w.qf[g], rem, lg, neg_m),
+          lt[g] += exp_chunk_shifted(chunk_scores<PREC, MASK>(kb, c, col, hf, w.qf[g], rem, lg, w.neg_m[g]),
                                      p16[g][c]);
       } else {
 #pragma unroll
@@ -282,6 +283,7 @@ __device__ __forceinline__ void attend_tile(WaveState<PREC, QG>& w, const unsign
         const float mnew = over ? fmaxf(w.m_run[g], mt) : w.m_run[g];
         const float alpha = __builtin_amdgcn_exp2f(w.m_run[g] - mnew);
         w.m_run[g] = mnew;
+        if constexpr (PREC == kPrecFp8) w.neg_m[g] = -mnew;
         w.l_run[g] *= alpha;
         w.o[g][0] *= alpha;
         w.o[g][1] *= alpha;
