@@ -309,6 +309,16 @@ __device__ __forceinline__ void attend_tile(WaveState<PREC, QG>& w, const unsign
       }
 }
 
+// s_setprio takes an immediate: one branch per level (p is wave-uniform).
+__device__ __forceinline__ void set_wave_priority(int p) {
+  switch (p) {
+    case 3: __builtin_amdgcn_s_setprio(3); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    default: __builtin_amdgcn_s_setprio(0); break;
+  }
+}
+
 template <int PREC, int QG, bool SPLIT, int W>
 __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
   typedef Ops<PREC> O;
@@ -323,10 +333,36 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 31, hf = lane >> 5;
-  const int bh = blockIdx.z;
+  // Workgroup -> (query-row block, KV split, b*H + h).  Workgroups are handed
+  // to the 8 XCDs round-robin (workgroup L runs on XCD L % 8), and each XCD
+  // has its own L2.  When several row blocks read the same split, XCD j takes
+  // the (split, head) units j, j + 8, ... and runs all row blocks of one unit
+  // back to back, so that they share the split's K/V in its L2; units past
+  // the last full group of 8 follow in plain order.
+  int rb = (int)blockIdx.x, sp = (int)blockIdx.y, bh = (int)blockIdx.z;
+  if constexpr (SPLIT) {
+    const int X = (int)gridDim.x;
+    if (X > 1) {
+      const int64_t U = (int64_t)gridDim.y * gridDim.z;
+      const int64_t L = blockIdx.x + (int64_t)X * (blockIdx.y + (int64_t)gridDim.y * blockIdx.z);
+      const int64_t ufull = U / 8 * 8;
+      int64_t u;
+      if (L < ufull * X) {
+        const int64_t j = L / 8;
+        rb = (int)(j % X);
+        u = (j / X) * 8 + L % 8;
+      } else {
+        const int64_t r = L - ufull * X;
+        rb = (int)(r % X);
+        u = ufull + r / X;
+      }
+      sp = (int)(u % gridDim.y);
+      bh = (int)(u / gridDim.y);
+    }
+  }
   const int b = bh / a.heads, h = bh - b * a.heads;
-  const int64_t q0 = (int64_t)blockIdx.x * QT;
-  const int split = (int)blockIdx.y + a.split_base;
+  const int64_t q0 = (int64_t)rb * QT;
+  const int split = sp + a.split_base;
   const int64_t n = a.n_b[b];                          // keys of this batch element
   const int64_t q_valid = a.ctx ? n : a.q_rows_valid;  // its valid query rows
 
@@ -452,6 +488,7 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
   // re-read its last tile), so the number of loads in flight is the same
   // everywhere and the wait before a store leaves the other set's loads
   // outstanding.
+  set_wave_priority(3);
   const int64_t t_last = t1 - 1;
   auto clamp = [&](int64_t t) { return t < t_last ? t : t_last; };
   Stage<EB, R> sa, sb;
@@ -478,13 +515,25 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
   else
     attend_tile<PREC, QG, true, true>(ws, kbuf[0], vbuf[0], lg, col, hf, rem_last);
   advance(t0, sa);  // for a one-tile range this stages an unused copy of the last tile
-  // tile t0+1+2i takes its successor from sb, tile t0+2+2i from sa
+  // tile t0+1+2i takes its successor from sb, tile t0+2+2i from sa.  The
+  // pairs of tiles run in four quarters of falling issue priority (3 down to
+  // 0): among the wavefronts sharing a SIMD the hardware favours the oldest,
+  // so without this a wavefront that started a moment later falls behind and
+  // finishes its last tiles alone, with no partner to overlap its MFMAs and
+  // its softmax; a wavefront that lags now keeps precedence until it reaches
+  // the next quarter.  Priority only orders issue; no result depends on it.
   int64_t t = t0 + 1;
-  for (; t + 1 < t_full; t += 2) {
-    attend_tile<PREC, QG, false, false>(ws, kbuf[1], vbuf[1], lg, col, hf, 64);
-    advance(t, sb);
-    attend_tile<PREC, QG, false, false>(ws, kbuf[0], vbuf[0], lg, col, hf, 64);
-    advance(t + 1, sa);
+  const int64_t pairs = t_full > t ? (t_full - t) / 2 : 0;
+#pragma unroll 1
+  for (int quarter = 0; quarter < 4; ++quarter) {
+    set_wave_priority(3 - quarter);
+    const int64_t t_q = t0 + 1 + 2 * (pairs * (quarter + 1) / 4);
+    for (; t < t_q; t += 2) {
+      attend_tile<PREC, QG, false, false>(ws, kbuf[1], vbuf[1], lg, col, hf, 64);
+      advance(t, sb);
+      attend_tile<PREC, QG, false, false>(ws, kbuf[0], vbuf[0], lg, col, hf, 64);
+      advance(t + 1, sa);
+    }
   }
   if (t < t_full) {
     attend_tile<PREC, QG, false, false>(ws, kbuf[1], vbuf[1], lg, col, hf, 64);
