@@ -43,3 +43,34 @@ def test_combine_chunk_boundaries(n, expect_splits):
     err = norm_err(whole[0], r.ref_query(np.arange(37)))
     say(f"  splits {info['kv_splits']}: normalised error {err:.2e}")
     assert err <= TOL[B.SDM_ICL_PREC_FP16]
+
+
+@pytest.mark.parametrize("base,prec", [("ctx16k_gated_fp16", B.SDM_ICL_PREC_FP8_E4M3),
+                                       ("ctx16k_log_fp16", B.SDM_ICL_PREC_FP16)])
+def test_xcd_order_with_a_partial_group_of_units(base, prec):
+    """Several query-row blocks per KV split run back to back on one XCD; with
+    3 heads the (split, head) units are not a multiple of 8, so the last ones
+    take the plain order.  300 query rows are 2 row blocks (FP8, 256 rows) or 3
+    (FP16, 128 rows) in one launch; the same rows queried as 137 + 163 are one
+    block per launch.  Both must agree bit for bit, and with the oracle."""
+    import torch
+    w = replace(gen.scaled_down(gen.WORKLOADS[base], 20000, 20000, 300), heads=3, seed=67, precision=prec,
+                name=f"xcd-tail-{prec}")
+    r = Run(w)
+    say("xcd order, partial group of units", base, prec)
+    cache, _ = r.fit(out_ctx=False)
+    try:
+        info = B.sdm_icl_attn_cache_info(cache)
+        units = info["kv_splits"] * 3
+        if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+            assert units % 8 != 0
+        whole = r.query(cache).cpu().numpy()
+        parts = np.concatenate([r.query(cache, (0, 137)).cpu().numpy(), r.query(cache, (137, 300)).cpu().numpy()],
+                               axis=1)
+        torch.cuda.synchronize()
+    finally:
+        cache.release()
+    np.testing.assert_array_equal(whole, parts)
+    err = norm_err(whole[0], r.ref_query(np.arange(300)))
+    say(f"  splits {info['kv_splits']} ({units} units): normalised error {err:.2e}")
+    assert err <= TOL[prec]
