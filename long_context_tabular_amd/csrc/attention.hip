@@ -251,11 +251,13 @@ __device__ __forceinline__ void attend_tile(WaveState<PREC, QG>& w, const unsign
       lt[g] = 0.f;
       if constexpr (PREC == kPrecFp8) {
         // the MFMA starts from -m, so it returns the logit minus the
-        // reference and P needs no per-score arithmetic before exp2
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          lt[g] += exp_chunk_shifted(chunk_scores<PREC, MASK>(kb, c, col, hf, w.qf[g], rem, lg, w.neg_m[g]),
-                                     p16[g][c]);
+        // reference and P needs no per-score arithmetic before exp2; both
+        // chunks' MFMAs are issued before the exponentials of the first, which
+        // then overlap the second's MFMA
+        const f32x16 s0 = chunk_scores<PREC, MASK>(kb, 0, col, hf, w.qf[g], rem, lg, w.neg_m[g]);
+        const f32x16 s1 = chunk_scores<PREC, MASK>(kb, 1, col, hf, w.qf[g], rem, lg, w.neg_m[g]);
+        lt[g] += exp_chunk_shifted(s0, p16[g][0]);
+        lt[g] += exp_chunk_shifted(s1, p16[g][1]);
       } else {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
