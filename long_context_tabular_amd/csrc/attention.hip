@@ -39,6 +39,11 @@
 //     is a separate instantiation.
 //   * O^T += V^T P^T with v_mfma_f32_32x32x16_f16; P is rounded to fp16
 //     (nearest even) and l is summed from the same rounded P (v_dot2).
+// Scheduling only (no result depends on it): split-KV launches run the row
+// blocks of one (split, head) back to back on one XCD so that they share its
+// K/V in that L2, and every wavefront lowers its issue priority by quarter of
+// its tile range, so that a wavefront that falls behind its SIMD partner
+// regains precedence.
 // Every per-row quantity depends only on that row's own scores, so a row's
 // result is independent of the other rows in the launch.
 #include <hip/hip_runtime.h>
