@@ -13,9 +13,15 @@
 //
 // Tiling: 128 x 128 output tiles, K in steps of 32; 4 wavefronts, each
 // 64 x 64 as 2 x 2 tiles of v_mfma_f32_32x32x16_f16.  Both operands are
-// K-contiguous, so the x and w tiles are staged into LDS the same way (rows of
-// 32 halves padded to 40), the next K step is loaded into registers while the
-// current one is multiplied, one barrier per step.  Workgroups are mapped to
+// K-contiguous, so the x and w tiles are staged into LDS the same way: global
+// loads that write LDS directly (no registers, no LDS store instructions)
+// into two stages, the next K step in flight while one is multiplied, one
+// barrier per step.  The kernel needs 100 VGPRs and 34 KB of LDS, so four
+// workgroups share a CU and cover each other's latency (measured faster than
+// deeper prefetch with fewer workgroups).  Staged rows are 64 bytes, unpadded; the
+// 16-byte chunk c of row r sits in slot c ^ ((r >> 2) & 3), which puts the 16
+// rows of one fragment read on 16 distinct bank groups (each lane fetches
+// the chunk that belongs in its fixed LDS slot).  Workgroups are mapped to
 // tiles so that the column tiles of one row tile run back to back on one XCD
 // and share the row tile in that XCD's L2.
 #include <hip/hip_runtime.h>
@@ -32,20 +38,28 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 128, kBN = 128, kBK = 32;
-constexpr int kDepth = 3;   // K steps loaded ahead into registers
-constexpr int kLRow = 40;   // LDS halves per staged row (32 + 8 pad)
+constexpr int kStages = 2;                      // LDS stages (K steps in flight: kStages - 1)
+constexpr int kRowB = kBK * 2;                  // bytes per staged row (64, unpadded)
+constexpr int kStageB = (kBM + kBN) * kRowB;    // 16 KB: the x tile, then the w tile
 constexpr int kCRow = 136;  // LDS halves per row of the output tile (128 + 8 pad)
-constexpr int kSmem = 2 * (kBM + kBN) * kLRow;  // operand stages; the output tile reuses them
-static_assert(kBM * kCRow <= kSmem, "output tile must fit in the operand stages");
+constexpr int kSmemB = kStages * kStageB > kBM * kCRow * 2 ? kStages * kStageB : kBM * kCRow * 2;
+static_assert(kBM * kCRow * 2 <= kSmemB, "output tile must fit in the operand stages");
+static_assert(kBM == 128 && kBN == 128 && kBK == 32, "the load mapping covers 16 rows per wave instruction");
+
+// LDS slot of the 16-byte chunk c (of 4) of staged row r; an involution in c
+__device__ __forceinline__ int chunk_slot(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+// wait until at most n vector-memory operations of this wave are outstanding
+// (gfx9 s_waitcnt encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4 and
+// lgkmcnt 11:8 left at their maxima)
+#define SDM_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
 
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void qkv_project_kernel(
     const _Float16* __restrict__ x, const _Float16* __restrict__ w, const _Float16* __restrict__ bias,
     int64_t M, int N, int K, int HD, int H, HeadFactors kh, const _Float16* __restrict__ gate,
     _Float16* __restrict__ q_out, _Float16* __restrict__ k_out, _Float16* __restrict__ v_out) {
-  __shared__ __attribute__((aligned(16))) _Float16 smem[kSmem];
-  auto as = [&](int buf) { return smem + buf * kBM * kLRow; };
-  auto bs = [&](int buf) { return smem + 2 * kBM * kLRow + buf * kBN * kLRow; };
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kSmemB];
   __shared__ float gate_u[kBM][2];  // gate factors of the tile's rows for its (at most) two heads
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -71,31 +85,27 @@ __global__ __launch_bounds__(256, 2) void qkv_project_kernel(
   const int n0 = (int)ct_ * kBN;
   const int64_t m0 = rt * kBM;
 
-  // staging chunk c = tid + 256 i: row c / 4 of the tile, 8 halves at k (c % 4) * 8;
-  // kDepth register sets hold the next K steps in flight
-  struct St { i32x4 a[2], b[2]; };
-  St ring[kDepth];
+  // Step kt's x and w tiles go to stage kt % kStages.  Wave wv, instruction i
+  // fills 16-row block 2 wv + i of each tile: lane l lands in row
+  // 16 (2 wv + i) + l / 4, slot l % 4, so it fetches that row's chunk
+  // chunk_slot(row, l % 4).  Rows past the end re-read the last row (their
+  // outputs are never stored), and steps past the last re-read it into a
+  // stage no later step reads, so that every wave always has the same number
+  // of loads in flight.
   const int nk = K / kBK;
-  auto load = [&](int kt, St& st) {
-    const int k0 = (kt < nk ? kt : nk - 1) * kBK;  // past the end: re-read the last step (unused)
+  auto load = [&](int kt) {
+    const int k0 = (kt < nk ? kt : nk - 1) * kBK;
+    unsigned char* st = smem + (kt % kStages) * kStageB;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i, r = c >> 2, kq = c & 3;
-      // rows past the end re-read the last row: every load is issued (a
-      // static count of loads in flight), and those rows only reach outputs
-      // past the end, which are never stored
+      const int blk = 2 * wv + i;
+      const int r = 16 * blk + (lane >> 2);
+      const int c = chunk_slot(r, lane & 3);
       const int64_t m = m0 + r;
       const int n = n0 + r;
-      st.a[i] = *reinterpret_cast<const i32x4*>(x + (m < M ? m : M - 1) * K + k0 + kq * 8);
-      st.b[i] = *reinterpret_cast<const i32x4*>(w + (int64_t)(n < N ? n : N - 1) * K + k0 + kq * 8);
-    }
-  };
-  auto store = [&](int buf, const St& st) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + 256 * i, r = c >> 2, kq = c & 3;
-      *reinterpret_cast<i32x4*>(&as(buf)[r * kLRow + kq * 8]) = st.a[i];
-      *reinterpret_cast<i32x4*>(&bs(buf)[r * kLRow + kq * 8]) = st.b[i];
+      __builtin_amdgcn_global_load_lds(x + (m < M ? m : M - 1) * K + k0 + c * 8, st + blk * 1024, 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(w + (int64_t)(n < N ? n : N - 1) * K + k0 + c * 8,
+                                       st + kBM * kRowB + blk * 1024, 16, 0, 0);
     }
   };
 
@@ -115,52 +125,50 @@ __global__ __launch_bounds__(256, 2) void qkv_project_kernel(
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  // step kt is multiplied from LDS buffer kt % 2 while steps kt+1 .. kt+kDepth
-  // are in flight in the register ring (slot (kt+1) % kDepth is stored at the
-  // end of step kt and refilled with step kt+1+kDepth)
-  load(0, ring[0]);
-  store(0, ring[0]);
+  // Step kt: wait for its own loads (issued kStages - 1 steps earlier; the 4
+  // loads of each later step may still be in flight), then a barrier that
+  // makes every wave's loads visible and frees the stage step kt - 1 was read
+  // from, which step kt + kStages - 1 then refills.
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d) load(1 + d, ring[d]);
-  __syncthreads();
-  auto step = [&](int kt, St& next) {
-    const int buf = kt & 1;
+  for (int d = 0; d < kStages - 1; ++d) load(d);
+  for (int kt = 0; kt < nk; ++kt) {
+    // an explicit wait and a bare s_barrier: __syncthreads() adds a fence
+    // that waits for every load in flight, which with more than two stages
+    // would drain the prefetch
+    SDM_WAIT_VMCNT(4 * (kStages - 2));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");  // the LDS stage was written behind the compiler's back
+    load(kt + kStages - 1);
+    const unsigned char* at = smem + (kt % kStages) * kStageB;
+    const unsigned char* bt = at + kBM * kRowB;
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
+      const int c = 2 * kk + (lane >> 5);
       f16x8 a[2], b[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        a[t] = *reinterpret_cast<const f16x8*>(&as(buf)[(wm * 64 + t * 32 + (lane & 31)) * kLRow + kk * 16 + 8 * (lane >> 5)]);
-        b[t] = *reinterpret_cast<const f16x8*>(&bs(buf)[(wn * 64 + t * 32 + (lane & 31)) * kLRow + kk * 16 + 8 * (lane >> 5)]);
+        const int ra = wm * 64 + t * 32 + (lane & 31);
+        const int rb = wn * 64 + t * 32 + (lane & 31);
+        a[t] = *reinterpret_cast<const f16x8*>(at + ra * kRowB + chunk_slot(ra, c) * 16);
+        b[t] = *reinterpret_cast<const f16x8*>(bt + rb * kRowB + chunk_slot(rb, c) * 16);
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) store(buf ^ 1, next);
-    // issued on every step (clamped past the end) so that the number of
-    // loads in flight is the same on every path and the wait before a store
-    // covers only that store's own step
-    load(kt + 1 + kDepth, next);
-    __syncthreads();
-  };
-  // the ring slot of step kt+1 is (kt % kDepth): unrolled by kDepth so that
-  // every slot index is a constant
-  int kt = 0;
-  for (; kt + kDepth <= nk; kt += kDepth) {
-#pragma unroll
-    for (int d = 0; d < kDepth; ++d) step(kt + d, ring[d]);
   }
-#pragma unroll
-  for (int d = 0; d < kDepth; ++d)
-    if (kt + d < nk) step(kt + d, ring[d]);
+  // the loads past the last step must land before the output tile reuses the
+  // stages, and every wave must be done reading them
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  asm volatile("" ::: "memory");
 
   // ---- epilogue.  Each lane holds column wn*64 + j*32 + lane%32 of 16 rows
   // per tile: bias, one fp16 rounding and the Q scaling are applied there and
   // the tile is assembled in LDS (the operand stages are free after the last
   // barrier), then written out as 16-byte row segments.
-  _Float16* const ct = smem;
+  _Float16* const ct = reinterpret_cast<_Float16*>(smem);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int cc = wn * 64 + j * 32 + (lane & 31);
