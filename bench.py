@@ -64,6 +64,81 @@ def counter_traffic(kernel: str):
     return None if v is None else int(float(v))
 
 
+PEAKS_SRC = os.path.join(ROOT, "bench_peaks.hip")
+PEAKS_LIB = os.path.join(ROOT, "bench_peaks.so")
+
+
+def build_peaks() -> str:
+    """Compile the peak probes (bench_peaks.hip) for gfx950 beside this file."""
+    import shutil
+    import subprocess
+    hipcc = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
+    tmp = PEAKS_LIB + ".tmp"
+    cmd = [hipcc, "-O3", "-std=c++17", "-fPIC", "-shared", "--offload-arch=gfx950",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", PEAKS_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"building {PEAKS_SRC} failed:\n{r.stderr}")
+    os.replace(tmp, PEAKS_LIB)
+    return PEAKS_LIB
+
+
+def measured_peaks() -> dict:
+    """Dense MFMA TFLOP/s (FP8 and FP16 loops, two wavefronts per SIMD) and HBM
+    streaming-read GB/s (0.5 and 4 GiB, once each) sustained on this GPU; the
+    best of three launches each."""
+    import ctypes
+    import torch
+    if not os.path.exists(PEAKS_LIB):
+        build_peaks()
+    lib = ctypes.CDLL(PEAKS_LIB)
+    lib.bench_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.bench_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p, ctypes.c_int,
+                                    ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+
+    def best_ms(go, reps=3):
+        go()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            go()
+            b.record()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        return min(times)
+
+    res = {}
+    blocks = cus * 2
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    for kind, name, flop, iters in ((0, "mfma_fp8_tflops", 131072, 20000), (1, "mfma_fp16_tflops", 32768, 40000)):
+        def go():
+            rc = lib.bench_peak_mfma(kind, blocks, iters, ctypes.c_void_p(out.data_ptr()), stream)
+            if rc != 0:
+                raise RuntimeError(f"bench_peak_mfma failed ({rc})")
+        ms = best_ms(go)
+        res[name] = round(blocks * 4 * iters * 4 * flop / (ms * 1e-3) / 1e12, 1)
+    rblocks = cus * 8
+    words = torch.empty(rblocks * 256, dtype=torch.int32, device="cuda")
+    for gib in (0.5, 4):
+        nbytes = int(gib * (1 << 30))
+        buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+        def go():
+            rc = lib.bench_peak_read(ctypes.c_void_p(buf.data_ptr()), nbytes // 16,
+                                     ctypes.c_void_p(words.data_ptr()), rblocks, stream)
+            if rc != 0:
+                raise RuntimeError(f"bench_peak_read failed ({rc})")
+        ms = best_ms(go)
+        res[f"hbm_read_GB_per_s_{gib:g}GiB"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+        del buf
+    torch.cuda.synchronize()
+    return res
+
+
 def dev(a):
     import numpy as np
     import torch
@@ -284,6 +359,8 @@ def main() -> int:
                     help="skip the host-offloaded (PCIe-streamed) cached queries")
     ap.add_argument("--no-model-call", action="store_true",
                     help="skip the model-call measurement (only the cached-prediction leg runs)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip measuring the sustained MFMA and HBM-read peaks")
     ap.add_argument("--cpu-sample-rows", type=int, default=384)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times) and exit; "
@@ -356,6 +433,14 @@ def main() -> int:
                      "launch_ms": round(ctx_avg, 4), "launches": ctx_n},
         "step_breakdown_ms": {k: round(v[0] / max(v[1], 1), 4) for k, v in t.items() if v[1]},
     }
+    peaks = None
+    if not args.no_peaks:
+        peaks = measured_peaks()
+        line["measured_peaks"] = peaks
+        mp = peaks["mfma_fp8_tflops" if info["precision"] == 1 else "mfma_fp16_tflops"]
+        line["roofline"]["measured_peak"] = mp
+        line["roofline"]["frac_of_measured"] = round(achieved / mp, 4)
+        log(f"[bench] measured peaks: {json.dumps(peaks)}")
     if not args.no_cached:
         wc = gen.WORKLOADS[args.cached_workload]
         log(f"[bench] cached prediction {wc.name}: n={wc.n_valid} batches {wc.query_batches}")
@@ -367,9 +452,14 @@ def main() -> int:
                           "batches": {str(k): {kk: (round(vv, 3) if isinstance(vv, float) else vv)
                                                for kk, vv in v.items()} for k, v in cres.items()},
                           "offloaded": cinfo.get("offloaded_queries")}
+        if peaks and r128:
+            line["cached"]["hbm_frac_of_measured"] = round(r128["GB_per_s"] / peaks["hbm_read_GB_per_s_4GiB"], 4)
         log(f"[bench] cached: {json.dumps(line['cached'])}")
     if not args.no_projection:
         line["projection"] = bench_projection(B, w)
+        if peaks:
+            line["projection"]["mfma_frac_of_measured"] = round(
+                line["projection"]["TFLOP_per_s"] / peaks["mfma_fp16_tflops"], 4)
         log(f"[bench] projection: {json.dumps(line['projection'])}")
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (float64 oracle)")
