@@ -85,8 +85,8 @@ def build_peaks() -> str:
 
 def measured_peaks() -> dict:
     """Dense MFMA TFLOP/s (FP8 and FP16 loops, two wavefronts per SIMD) and HBM
-    streaming-read GB/s (0.5 and 4 GiB, once each) sustained on this GPU; the
-    best of three launches each."""
+    streaming-read GB/s (0.5 and 4 GiB, once each, 32 workgroups per CU)
+    sustained on this GPU; the best of three launches each."""
     import ctypes
     import torch
     if not os.path.exists(PEAKS_LIB):
@@ -121,7 +121,7 @@ def measured_peaks() -> dict:
                 raise RuntimeError(f"bench_peak_mfma failed ({rc})")
         ms = best_ms(go)
         res[name] = round(blocks * 4 * iters * 4 * flop / (ms * 1e-3) / 1e12, 1)
-    rblocks = cus * 8
+    rblocks = cus * 32
     words = torch.empty(rblocks * 256, dtype=torch.int32, device="cuda")
     for gib in (0.5, 4):
         nbytes = int(gib * (1 << 30))

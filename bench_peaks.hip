@@ -9,8 +9,9 @@
 //                    v_mfma_f32_32x32x16_f16, 32,768 FLOP each); 256-thread
 //                    blocks; `out` holds one float per thread.
 //   bench_peak_read  streams `n16` 16-byte elements of `src` once (grid-stride,
-//                    four loads in flight per thread); `out` holds one word
-//                    per thread.
+//                    eight non-temporal loads in flight per thread: the
+//                    fastest of the variants tried); `out` holds one word per
+//                    thread.
 // Both return the launch's hipError_t.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -64,9 +65,12 @@ __global__ __launch_bounds__(256) void read_loop(const i32x4* __restrict__ src, 
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   i32x4 x = {0, 0, 0, 0};
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    const i32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
-    x ^= a ^ b ^ c ^ d;
+  for (; i + 7 * stride < n; i += 8 * stride) {
+    i32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x ^= v[u];
   }
   for (; i < n; i += stride) x ^= src[i];
   out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = (unsigned)(x[0] ^ x[1] ^ x[2] ^ x[3]);
