@@ -225,9 +225,10 @@ __device__ __forceinline__ f32x16 chunk_scores(const unsigned char* kb, int c, i
 // One 64-key tile for all QG groups of the wave.  FIRST: the first tile of
 // the wave's KV range, which sets the reference maximum.  MASK: the tile holds
 // keys >= n (only the last tile of the context can), 'rem' = n - tile start.
-// Each 32-key chunk's scores are turned into P as soon as its MFMA returns,
-// so only one chunk of scores is live; the rare overflow path recomputes
-// the scores instead of keeping them.
+// FP16 turns each 32-key chunk's scores into P as soon as its MFMAs return
+// (one chunk of scores live); FP8 issues both chunks' MFMAs of a group first
+// (two live), so that the first chunk's exponentials overlap the second's
+// MFMA.  The rare overflow path recomputes the scores instead of keeping them.
 template <int PREC, int QG, bool FIRST, bool MASK>
 __device__ __forceinline__ void attend_tile(WaveState<PREC, QG>& w, const unsigned char* kb,
                                             const unsigned char* vb, Logit lg, int col,
