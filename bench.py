@@ -37,9 +37,11 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
+    """sha256 (first 16 hex digits) of the attention kernels' sources and of
+    build_lib.py, which holds their compiler flags."""
     h = hashlib.sha256()
-    for f in ("attention.hip", "prep.hip", "scaling.h"):
-        with open(os.path.join(ROOT, "long_context_tabular_amd", "csrc", f), "rb") as fh:
+    for f in ("csrc/attention.hip", "csrc/prep.hip", "csrc/scaling.h", "build_lib.py"):
+        with open(os.path.join(ROOT, "long_context_tabular_amd", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 

@@ -19,9 +19,10 @@ CSRC = os.path.join(PKG, "csrc")
 LIB_NAME = "libsdm_icl_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["prep.hip", "attention.hip", "projection.hip", "sdm_icl_attn.cpp"]
-# per-source flags: the attention kernels schedule for instruction-level
-# parallelism (measured ~5% faster on the 512K context pass)
-EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+# per-source flags: the attention kernels use LLVM's iterative
+# maximum-occupancy machine scheduler (measured 2.6% faster on the 512K
+# context pass than the max-ILP strategy, itself ~5% faster than the default)
+EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-maxocc"]}
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-ffp-contract=off",
