@@ -173,9 +173,16 @@ def _c_scope():
 
 
 def _stream_ptr(stream) -> Optional[int]:
+    """The HIP stream handle to pass: the given torch stream, else the current
+    stream of the current device (read through torch's raw accessor when it
+    exists: the public call builds a Stream object, ~3 us per query)."""
     import torch
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream or None
+    if stream is None:
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:
+            return raw(torch.cuda.current_device()) or None
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream or None
 
 
 def _dev_ptr(t, name: str, dtype=None) -> Optional[int]:
@@ -332,8 +339,8 @@ def sdm_icl_attn_query(cache: Cache, q, gate=None, out=None, workspace=None, str
         out = torch.empty_like(q)
     elif tuple(out.shape) != (B, R, H, D):
         raise ValueError("out must have the shape of q")
-    need = sdm_icl_attn_query_workspace_size(cache, R)
     if workspace is None:
+        need = sdm_icl_attn_query_workspace_size(cache, R)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size()
     with _c_scope():
