@@ -337,8 +337,16 @@ def cpu_baseline(gen, x, w, sample_rows: int):
     icl.attend(cache, x.q_query[0, qrows], x.gate_query[0, qrows] if gated else None)
     dt = time.perf_counter() - t0
     flops = 4.0 * (rows.size + qrows.size) * w.n_valid * w.head_dim * w.heads
+    rows_per_s = (rows.size + qrows.size) / dt
+    # every row costs the same (all keys, all heads), so the whole model call's
+    # rows (n context + R query) take n_rows / rows_per_s at this rate
+    full_rows = w.n_valid + w.n_query
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "seconds": round(dt, 3), "fit_seconds_untimed": round(t_fit, 3),
+            "rows_per_s": round(rows_per_s, 2),
+            "extrapolated_full_call_s": round(full_rows / rows_per_s, 1),
+            "extrapolation": (f"linear in rows: {full_rows} rows (the {w.n_valid} valid context rows and {w.n_query} "
+                              f"queries) at the sampled rows/s, excluding the fit"),
             "host_cpus": len(os.sched_getaffinity(0)),
             "sample": (f"{rows.size} context rows (incl. first/last 8 valid) + {qrows.size} query rows of "
                        f"{w.name}, each against all {w.n_valid} keys x {w.heads} heads, float64; the "
