@@ -676,11 +676,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, int prec, bool split, hipStream_t s, int grid_splits) {
-  // FP8 takes two 32-row query groups per wavefront (more MFMA work per LDS
-  // read and per softmax step); split-KV calls with at most 128 rows use
-  // two-wavefront workgroups so that one small query batch still fills the
-  // chip.  FP16 keeps one group per wavefront (its Q fragment is twice as
-  // large).
+  // Context passes of more than 128 rows take two 32-row query groups per
+  // wavefront (more MFMA work per LDS read and per softmax step); for FP16
+  // the larger Q fragments push that kernel to the register limit, with a
+  // few spills outside its tile loop, and it is still ~10% faster than one
+  // group.  FP8 split-KV calls take two groups too, with two-wavefront
+  // workgroups at most 128 rows so that one small query batch still fills
+  // the chip; FP16 split-KV calls keep one group (two measured slower).
   const int64_t rows = split ? a.q_rows_valid : a.out_rows;
   auto go = [&](auto kern, int qt, int waves) {
     const dim3 grid((unsigned)((rows + qt - 1) / qt), (unsigned)(grid_splits > 0 ? grid_splits : a.splits),
@@ -697,7 +699,8 @@ hipError_t launch_attention(const AttnArgs& a, int prec, bool split, hipStream_t
     }
   } else {
     if (split) go(attention_kernel<kPrecFp16, 1, true, 4>, 128, 4);
-    else go(attention_kernel<kPrecFp16, 1, false, 4>, 128, 4);
+    else if (a.q_rows_valid <= 128) go(attention_kernel<kPrecFp16, 1, false, 4>, 128, 4);
+    else go(attention_kernel<kPrecFp16, 2, false, 4>, 256, 4);
   }
   return hipGetLastError();
 }
