@@ -609,6 +609,44 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// Lane (g, j)'s normalised partial outputs of splits s0 + g + 4i (i < 16) of
+// one (b, h, row), d in [4j, 4j + 4).  Slots past the last split re-read the
+// last split (the caller skips them): unconditional loads, so that none of
+// them sits behind a branch that waits for the others.
+__device__ __forceinline__ void load_partials(const uint16_t* po, int s0, int splits, int g, int j,
+                                              f16x4 (&o)[16]) {
+  const int cnt = splits - s0 < 64 ? splits - s0 : 64;
+  const f16x4* pos = reinterpret_cast<const f16x4*>(po + (int64_t)s0 * 64) + j;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int s = g + 4 * i;
+    o[i] = pos[(s < cnt ? s : cnt - 1) * 16];
+  }
+}
+
+// One 64-split chunk of a row: lane s0 + lane's weight w = 2^(m_s - M) l_s,
+// then acc += w_s (O_s / l_s) over the lane's splits s = g + 4i in increasing
+// order; returns the chunk's sum of weights (a fixed butterfly).
+__device__ __forceinline__ float combine_chunk(const float* ml, int s0, int splits, float m, int lane, int g,
+                                               const f16x4 (&o)[16], f32x4& acc) {
+  const int sl = s0 + lane;
+  const int sc = sl < splits ? sl : splits - 1;
+  const float ms = ml[2 * sc], ls = ml[2 * sc + 1];
+  const float wl = sl < splits ? __builtin_amdgcn_exp2f(ms - m) * ls : 0.f;
+  const float lsum = wave_sum(wl);
+  const int cnt = splits - s0 < 64 ? splits - s0 : 64;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int s = g + 4 * i;
+    const float ws = __shfl(wl, s, 64);
+    if (s < cnt) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(ws, (float)o[i][e], acc[e]);
+    }
+  }
+  return lsum;
+}
+
 // One wavefront per (b, h, row); splits are taken 64 at a time.  Lane s of
 // a chunk owns split s for the maximum M and the weight
 // w_s = exp2(m_s - M) * l_s of its normalised output O_s / l_s (fp16); the
@@ -633,31 +671,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   const int g = lane >> 4, j = lane & 15;
   float l = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // The first chunk's partial outputs do not depend on the maximum: their
+  // loads are issued first, together with the (m, l) loads, so that the two
+  // share one memory round trip.  The order of every sum is the same as one
+  // chunk at a time.
+  f16x4 o[16];
+  load_partials(po, 0, splits, g, j, o);
+  // (m, l) loads are unconditional too (clamped to the last split, the
+  // value then discarded)
   float m = -INFINITY;
-  for (int s0 = 0; s0 < splits; s0 += 64)
-    if (s0 + lane < splits) m = fmaxf(m, ml[2 * (s0 + lane)]);
-  m = wave_max(m);
   for (int s0 = 0; s0 < splits; s0 += 64) {
     const int sl = s0 + lane;
-    const float wl = sl < splits ? __builtin_amdgcn_exp2f(ml[2 * sl] - m) * ml[2 * sl + 1] : 0.f;
-    l += wave_sum(wl);
-    const int cnt = splits - s0 < 64 ? splits - s0 : 64;
-    const f16x4* pos = reinterpret_cast<const f16x4*>(po + (int64_t)s0 * 64) + j;
-    f16x4 o[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int s = g + 4 * i;
-      o[i] = s < cnt ? pos[s * 16] : f16x4{};
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int s = g + 4 * i;
-      const float ws = __shfl(wl, s, 64);
-      if (s < cnt) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(ws, (float)o[i][e], acc[e]);
-      }
-    }
+    const float ms = ml[2 * (sl < splits ? sl : splits - 1)];
+    if (sl < splits) m = fmaxf(m, ms);
+  }
+  m = wave_max(m);
+  for (int s0 = 0; s0 < splits; s0 += 64) {
+    if (s0 > 0) load_partials(po, s0, splits, g, j, o);
+    l += combine_chunk(ml, s0, splits, m, lane, g, o, acc);
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
