@@ -117,6 +117,9 @@ CASES = [
     ("cached512k_fp8_gated", 2048, 2048, 129),
     ("ctx128k_fp8", 128, 100, 40),              # FP8 context of <= 128 rows (one group per wavefront)
     ("model512k_fp8_log", 320, 129, 1),         # 129 rows: one key in the last tile, one query row
+    ("ctx16k_log_fp16", 128, 100, 40),          # FP16 context of <= 128 rows (one group per wavefront)
+    ("ctx16k_gated_fp16", 320, 129, 3),         # FP16, two groups: one key in the last tile, one valid row
+                                                # in the second wavefront's block
 ]
 
 
