@@ -158,7 +158,10 @@ sdm_icl_status sdm_icl_attn_query_workspace_size(sdm_icl_cache cache, int64_t n_
  * and never synchronises.  The result of a row is bitwise independent of R
  * and of the other rows in the call (fixed KV split plan, fixed combine
  * order, context-derived Q scale).  R == 0 is a no-op.  Concurrent calls on
- * one cache with distinct workspaces are safe. */
+ * one cache with distinct workspaces are safe.  On a resident (not
+ * offloaded) cache the call enqueues only kernel launches on `stream` (with
+ * kernel timing off), so it can be captured into a graph and replayed; the
+ * graph reads q, gate and the cache when it runs. */
 sdm_icl_status sdm_icl_attn_query(sdm_icl_cache cache, const void* q, const void* gate,
                                   int64_t n_query, void* out, void* workspace,
                                   size_t workspace_bytes, void* stream);
