@@ -282,9 +282,11 @@ def bench_cached(B, gen, w, reps, offload=True):
     return res, info
 
 
-def bench_projection(B, w, reps: int = 5):
+def bench_projection(B, w, reps: int = 21, warmup: int = 10):
     """The fused Q/K/V projection at the model-call size: hidden rows
-    [1, n_pad, H*64] times a [3*H*64, H*64] weight, LogScale on Q."""
+    [1, n_pad, H*64] times a [3*H*64, H*64] weight, LogScale on Q.  Median of
+    `reps` calls after `warmup` (enough for the clock to settle after the
+    cached leg's short bursts)."""
     import numpy as np
     import torch
     g = torch.Generator(device="cuda").manual_seed(w.seed)
@@ -296,7 +298,7 @@ def bench_projection(B, w, reps: int = 5):
     outs = tuple(torch.empty((1, w.n_pad, w.heads, w.head_dim), dtype=torch.float16, device="cuda") for _ in range(3))
     run = lambda: B.sdm_icl_qkv_project(x, wt, bias, heads=w.heads, key_length=w.n_valid, head_coef=coef,
                                         scale_mode=B.SDM_ICL_SCALE_LOG, outs=outs)
-    for _ in range(2):
+    for _ in range(warmup):
         run()
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
