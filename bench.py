@@ -188,7 +188,7 @@ def bench_model_call(B, gen, w, steps, warmup):
     return x, info, (t1 - t0) / steps, timings
 
 
-def bench_cached(B, gen, w, reps, offload=True):
+def bench_cached(B, gen, w, reps, offload=True, warmup=300):
     import numpy as np
     import torch
     x = gen.make_inputs(w)
@@ -207,7 +207,7 @@ def bench_cached(B, gen, w, reps, offload=True):
         qbs = [qq[:, i * R:(i + 1) * R].contiguous() for i in range(nb)]
         gbs = [gq[:, i * R:(i + 1) * R].contiguous() if gq is not None else None for i in range(nb)]
         obs = [torch.empty_like(qb) for qb in qbs]
-        for _ in range(10):
+        for _ in range(warmup):
             B.sdm_icl_attn_query(cache, qbs[0], gbs[0], out=obs[0], workspace=ws)
         torch.cuda.synchronize()
         # (1) one call at a time: the latency a single predict batch sees
@@ -363,6 +363,9 @@ def main() -> int:
     ap.add_argument("--workload", default="model512k_fp8_log")
     ap.add_argument("--cached-workload", default="cached512k_fp8_gated")
     ap.add_argument("--cached-reps", type=int, default=30)
+    ap.add_argument("--cached-warmup", type=int, default=300,
+                    help="untimed query calls per batch size before its timed calls (ten 128-row calls, about "
+                         "2 ms of GPU work, leave the clocks below their steady state)")
     ap.add_argument("--no-cached", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-projection", action="store_true",
@@ -404,7 +407,8 @@ def main() -> int:
 
     if args.no_model_call:
         wc = gen.WORKLOADS[args.cached_workload]
-        cres, cinfo = bench_cached(B, gen, wc, args.cached_reps, offload=not args.no_offload)
+        cres, cinfo = bench_cached(B, gen, wc, args.cached_reps, offload=not args.no_offload,
+                                   warmup=args.cached_warmup)
         print(json.dumps({"cached": {"workload": wc.name, "kv_splits": cinfo["kv_splits"],
                                      "batches": {str(k): v for k, v in cres.items()}}}), flush=True)
         return 0
@@ -458,7 +462,8 @@ def main() -> int:
     if not args.no_cached:
         wc = gen.WORKLOADS[args.cached_workload]
         log(f"[bench] cached prediction {wc.name}: n={wc.n_valid} batches {wc.query_batches}")
-        cres, cinfo = bench_cached(B, gen, wc, args.cached_reps, offload=not args.no_offload)
+        cres, cinfo = bench_cached(B, gen, wc, args.cached_reps, offload=not args.no_offload,
+                                   warmup=args.cached_warmup)
         r128 = cres.get(128)
         line["cached"] = {"workload": wc.name, "kv_splits": cinfo["kv_splits"],
                           "GB_per_s": round(r128["GB_per_s"], 1) if r128 else None,
