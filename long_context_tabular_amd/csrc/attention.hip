@@ -235,6 +235,10 @@ __device__ __forceinline__ void attend_tile(WaveState<PREC, QG>& w, const unsign
                                             int hf, int rem) {
   const float c_scale = lg.c;
   f16x8 p16[QG][2][2];
+  // FP8: ask the scheduler to interleave the MFMAs with the tile's other
+  // instructions in small groups (a scheduling hint only; it made the FP8
+  // context pass faster and the FP16 one slower, so FP16 goes without)
+  if constexpr (PREC == kPrecFp8) __builtin_amdgcn_iglp_opt(0);
   if constexpr (FIRST) {
 #pragma unroll
     for (int g = 0; g < QG; ++g) {
@@ -303,6 +307,7 @@ __device__ __forceinline__ void attend_tile(WaveState<PREC, QG>& w, const unsign
   }
 
   // ---- O^T += V^T P^T
+  if constexpr (PREC == kPrecFp8) __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
   for (int c = 0; c < 2; ++c)
 #pragma unroll
