@@ -17,7 +17,8 @@ Contents
               quantisation ("[FP8 3/4] Integrate FP8 attention and caching into
               TabICLv2", introduction), and non-causal row-wise attention of
               context rows and of query rows against the context K/V (same
-              page: shared attention projects Q/K/V and falls back to SDPA).
+              page, walkthrough: one shared projection, then PyTorch's
+              scaled dot-product attention).
 
 Every function cites the passage it follows.  Where the pages leave a step
 open, the reading taken is stated in the function's docstring.

@@ -3,17 +3,18 @@
 Sources (page titles as printed on the pages):
 
 * "Fuse shared-length query scaling during inference" -- Problem identified:
-  LogScale multiplies queries by a per-head coefficient times the log of a
-  shared key length; GatedLogScale adds a tanh gate through separate tanh,
-  addition and multiplication passes.  Solution: the length arithmetic is
-  float32 and every eager dtype-rounding boundary is preserved.  Summary
-  (sequence diagram): the eager path applies *clamped* log scaling.
+  the LogScale factor of a head is its coefficient times the log of the key
+  length all rows share; the gated variant also takes tanh of a gate, adds
+  one and multiplies, each as its own eager step.  Solution: the length is
+  handled in float32 and each intermediate keeps the dtype rounding the
+  eager code gives it.  Summary (sequence diagram): the log is clamped.
 * "[FP8 3/4] Integrate FP8 attention and caching into TabICLv2" -- intro:
   Q/K/V of intermediate ICL layers are quantised to FP8 above 8,192 unmasked
   context rows; Q scales are derived from the context so cached prediction
   does not depend on how queries are batched; ``model.fit`` builds the cache
-  and ``model.predict`` reuses it; shared attention projects Q/K/V and falls
-  back to SDPA (scaled dot-product attention, scale 1/sqrt(head_dim)).
+  and ``model.predict`` reuses it.  Walkthrough: Q/K/V come from one shared
+  projection and the attention itself is PyTorch's scaled dot-product
+  attention (softmax scale 1/sqrt(head_dim)).
 
 Readings where the pages are silent (each is a choice, listed with its
 reason in the design notes of the repository):
@@ -23,19 +24,13 @@ reason in the design notes of the repository):
 * LogScale: ``q~ = fp16(q * k_h)``.  GatedLogScale:
   ``q~ = fp16(fp16(q * k_h) * fp16(1 + fp16(tanh g)))`` with one gate value
   per row and head.
-* FP8 scales per (batch, head) from the amax over valid rows: for K and V
-  ``s = fp32(a / 448)``, ``inv = fp32(448 / a)`` (a = 0 gives s = inv = 1);
-  codes are ``e4m3(clamp(fp32(x * inv), +-448))``.  The Q scale comes from
-  the *scaled* context queries (query rows reuse it and saturate above it)
-  and is the smallest one for which the logit of one unit of
-  ``sum_d q_code k_code`` is a power of two: with ``base = fp32(fp32(log2(e)
-  / sqrt(D)) * s_k)``, ``inv_q = base * 2^-E`` for the smallest integer E
-  with ``fp32(a_q * base) <= 448 * 2^E``, and the logit in log2 units is
-  ``2^E * sum_d q_code k_code`` exactly (``q_unit = 2^E`` is kept where the
-  Q scale would be; the dequantised Q scale is ``2^E ln 2 / (tau s_k)``).
-  The pages only ask for a context-derived Q scale; e4m3 is a floating-point
-  format, so the factor in [1, 2) this costs shifts Q's range by less than
-  one binade and leaves its relative precision unchanged.
+* FP8 scales per (batch, head) from the amax over valid rows, the same rule
+  for Q, K and V: ``s = fp32(a / 448)``, ``inv = fp32(448 / a)`` (a = 0
+  gives s = inv = 1); codes are ``e4m3(clamp(fp32(x * inv), +-448))`` and
+  the dequantised operand is ``code * s``.  Q's amax is taken over the
+  *scaled* context queries (what is quantised); query rows reuse the
+  context's Q scale and saturate above it, so a query row's result does not
+  depend on the other rows of its batch.
 * masked context rows (index >= n) are not keys, not part of n and not part
   of any amax; their outputs are zero.
 * per-batch lengths (the pages' fused path covers one shared int and falls
@@ -138,31 +133,6 @@ def fp8_scale(amax) -> tuple:
     if a == 0:
         return np.float32(1.0), np.float32(1.0)
     return np.float32(a / np.float32(E4M3_MAX)), np.float32(np.float32(E4M3_MAX) / a)
-
-
-def log2e_tau_f32(head_dim: int = 64) -> np.float32:
-    """float32 of log2(e) / sqrt(D): the base-2 logit factor of SDPA."""
-    return np.float32(1.4426950408889634 / math.sqrt(head_dim))
-
-
-def fp8_query_scale(amax_q, s_k, head_dim: int = 64) -> tuple:
-    """(q_unit = 2^E, inv_q) in float32 for one (batch, head) of the Q operand.
-
-    ``base = fp32(fp32(log2 e / sqrt D) * s_k)``; E is the smallest integer
-    with ``fp32(amax_q * base) <= 448 * 2^E`` (E = 0 for an all-zero Q), and
-    ``inv_q = base * 2^-E``, so the amax quantises to at most 448 and the
-    logit of one unit of sum_d q_code k_code is exactly 2^E in log2 units."""
-    base = np.float32(log2e_tau_f32(head_dim) * np.float32(s_k))
-    a = np.float32(amax_q)
-    e = 0
-    if a != 0:
-        v = float(np.float32(a * base))
-        e = math.ceil(math.log2(v / E4M3_MAX))
-        while math.ldexp(E4M3_MAX, e) < v:
-            e += 1
-        while math.ldexp(E4M3_MAX, e - 1) >= v:
-            e -= 1
-    return np.float32(math.ldexp(1.0, e)), np.float32(math.ldexp(float(base), -e))
 
 
 def amax_rows(x: np.ndarray) -> np.ndarray:
@@ -293,15 +263,11 @@ class OracleCache:
         return self.v16[b][:, h, :].astype(np.float64)
 
     def qhat(self, qt: np.ndarray, b: int, h: int) -> np.ndarray:
-        """Operand used for scaled query rows qt ``[m, H, D]`` (fp16) of head h.
-
-        FP8: the codes times the dequantised Q scale ``q_unit ln 2 / (tau
-        s_k)``, so that tau * qhat . khat = q_unit * ln 2 * sum of code
-        products, i.e. 2^E * sum in log2 units."""
+        """Operand used for scaled query rows qt ``[m, H, D]`` (fp16) of head h:
+        FP8 quantises with the context's Q scale and dequantises with it."""
         x = qt[:, h, :]
         if self.precision == PREC_FP8_E4M3:
-            s_q = np.float64(self.scales[0, b, h]) * math.log(2.0) / (self.tau * np.float64(self.scales[1, b, h]))
-            return quantize(x, self.inv[0, b, h]) * s_q
+            return quantize(x, self.inv[0, b, h]) * np.float64(self.scales[0, b, h])
         return x.astype(np.float64)
 
 
@@ -348,9 +314,6 @@ def fit(q: np.ndarray, k: np.ndarray, v: np.ndarray, n, scale_mode: int,
                 a = amax_rows(x)
                 for h in range(H):
                     scales[t, b, h], inv[t, b, h] = fp8_scale(a[h])
-            a = amax_rows(qt)
-            for h in range(H):
-                scales[0, b, h], inv[0, b, h] = fp8_query_scale(a[h], scales[1, b, h], D)
             kc = np.empty((H, nb, D), dtype=np.uint8)
             vc = np.empty((H, nb, D), dtype=np.uint8)
             for h in range(H):
@@ -402,7 +365,7 @@ def context_outputs(cache: OracleCache, q: np.ndarray, gate: Optional[np.ndarray
 # ---------------------------------------------------------------------------
 # The shared Q/K/V projection, with the query scaling applied to its output
 # ("[FP8 3/4] Integrate FP8 attention and caching into TabICLv2", walkthrough:
-# shared attention projects Q/K/V before attending; "Fuse shared-length query
+# one shared projection makes Q, K and V before attention; "Fuse shared-length query
 # scaling during inference", Solution: the scaling joins the producer of q
 # instead of running as separate passes over it)
 # ---------------------------------------------------------------------------

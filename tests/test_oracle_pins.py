@@ -372,54 +372,65 @@ def test_fused_projection_scaling_is_the_separate_pass():
     assert not np.array_equal(qs, q)
 
 
-def test_fp8_grid_inputs_and_the_query_scale_rule():
-    """I10, restated for the Q scale rule.  K and V on the e4m3 grid with
-    amax = 448 s (each tensor and head its own power-of-two scale) quantise
-    losslessly, so a mixed-up K/V scale changes the result.  The Q scale:
-    q_unit is a power of two, the Q amax lands in (224, 448] once scaled (E is
-    the smallest exponent that keeps it in range), and inv_q * q_unit is the
-    rule's base fp32(fp32(log2 e / 8) * s_k).  The output equals a softmax in
-    base 2 over 2^E * (sum of code products), computed here straight from the
-    codes (so the ln 2 / tau bookkeeping of the dequantised operands is
-    checked by a different route)."""
+def test_fp8_is_lossless_on_grid_inputs():
+    """I10: when Q~, K and V already lie on the e4m3 grid with amax = 448 s,
+    FP8 quantisation changes nothing and the FP8 result equals the FP16 one
+    exactly.  Each tensor and head gets its own power-of-two scale, so a
+    mixed-up scale (s_k used for Q or V, a dropped Q scale) changes the
+    result; the codes and scales are checked against the grid they came from."""
     rng = np.random.default_rng(3)
     B, N, H, D = 1, 96, 2, 64
     grid = numerics.E4M3_VALUES[np.isfinite(numerics.E4M3_VALUES)]
     grid = grid[np.abs(grid) <= 64]
     scales = {"q": (2.0 ** -9, 2.0 ** -8), "k": (2.0 ** -10, 2.0 ** -7), "v": (2.0 ** -6, 2.0 ** -11)}
+    drawn = {}
+
     def draw(name):
         t = np.empty((B, N, H, D))
+        codes = np.empty((B, N, H, D))
         for h in range(H):
             s = scales[name][h]
-            t[0, :, h] = rng.choice(grid, size=(N, D)) * s
-            t[0, 0, h, 0] = 448 * s          # pin amax to 448 s in every head
+            codes[0, :, h] = rng.choice(grid, size=(N, D))
+            codes[0, 0, h, 0] = 448                       # pin amax to 448 s in every head
+            t[0, :, h] = codes[0, :, h] * s
         assert np.all(t.astype(np.float16).astype(np.float64) == t)   # fp16-exact
+        drawn[name] = codes
         return t.astype(np.float16)
+
     q, k, v = draw("q"), draw("k"), draw("v")
     c8 = icl.fit(q, k, v, N, icl.SCALE_NONE, icl.PREC_FP8_E4M3)
-    for t, name in ((1, "k"), (2, "v")):
+    c16 = icl.fit(q, k, v, N, icl.SCALE_NONE, icl.PREC_FP16)
+    for t, name in enumerate("qkv"):
         np.testing.assert_array_equal(c8.scales[t, 0], np.float32(scales[name]))
-    np.testing.assert_array_equal(numerics.E4M3_VALUES[c8.k_codes[0]] * np.array(scales["k"])[:, None, None],
-                                  k[0].transpose(1, 0, 2).astype(np.float64))
-    np.testing.assert_array_equal(numerics.E4M3_VALUES[c8.v_codes[0]] * np.array(scales["v"])[:, None, None],
-                                  v[0].transpose(1, 0, 2).astype(np.float64))
-    base_const = np.float32(1.4426950408889634 / 8)
-    rows = np.arange(N)
-    got = icl.context_outputs(c8, q, None, rows)
+        np.testing.assert_array_equal(c8.inv[t, 0], np.float32(1.0 / np.array(scales[name])))
+    np.testing.assert_array_equal(numerics.E4M3_VALUES[c8.k_codes[0]], drawn["k"][0].transpose(1, 0, 2))
+    np.testing.assert_array_equal(numerics.E4M3_VALUES[c8.v_codes[0]], drawn["v"][0].transpose(1, 0, 2))
     for h in range(H):
-        qu, inv = c8.scales[0, 0, h], c8.inv[0, 0, h]
-        mant, ex = np.frexp(np.float64(qu))
-        assert mant == 0.5                                            # a power of two
-        base = np.float32(base_const * np.float32(scales["k"][h]))
-        assert np.float64(inv) * np.float64(qu) == np.float64(base)
-        top = np.float32(np.float32(448 * scales["q"][h]) * inv)      # the amax element, scaled
-        assert 224 < top <= 448
-        qc = numerics.e4m3_round(np.clip(q[0, :, h].astype(np.float32) * inv, -448, 448).astype(np.float32))
-        kc = numerics.E4M3_VALUES[c8.k_codes[0, h]]
-        logit2 = np.float64(qu) * (qc.astype(np.float64) @ kc.T)       # log2 units
-        w = np.exp2(logit2 - logit2.max(axis=1, keepdims=True))
-        want = (w @ v[0, :, h].astype(np.float64)) / w.sum(axis=1, keepdims=True)
-        np.testing.assert_allclose(got[:, h], want, rtol=0, atol=1e-12 * np.abs(want).max())
+        np.testing.assert_array_equal(c8.qhat(q[0], 0, h), q[0, :, h].astype(np.float64))
+    rows = np.arange(N)
+    ref = icl.context_outputs(c16, q, None, rows)
+    np.testing.assert_array_equal(icl.context_outputs(c8, q, None, rows), ref)
+    # the same rows as queries of the fitted cache
+    np.testing.assert_array_equal(icl.attend(c8, q[0], None), icl.attend(c16, q[0], None))
+
+
+def test_fp8_query_codes_are_the_plain_per_head_quantisation():
+    """The Q operand of the FP8 path is the scaled query quantised with the
+    context's own per-head scale: its dequantised values are within 2^-4
+    relative of q~ (the e4m3 bound) and the amax element lands on +-448."""
+    x = _small("model512k_fp8_log", 2048, n_query=8)
+    w = x.workload
+    c = icl.fit(x.q_ctx, x.k_ctx, x.v_ctx, w.n_valid, icl.SCALE_LOG, icl.PREC_FP8_E4M3, x.head_coef)
+    qt = icl.scale_queries(x.q_ctx[0, :w.n_valid], icl.SCALE_LOG, c.k_h)
+    for h in range(w.heads):
+        ref = qt[:, h].astype(np.float64)
+        a = np.max(np.abs(ref))
+        assert c.scales[0, 0, h] == np.float32(np.float32(a) / np.float32(448))
+        got = c.qhat(qt, 0, h)
+        s = float(c.scales[0, 0, h])
+        big = np.abs(ref) >= 2.0 ** -6 * s
+        assert np.all(np.abs(got - ref)[big] <= np.abs(ref)[big] * 2.0 ** -4 * (1 + 1e-6))
+        assert np.max(np.abs(got)) == 448.0 * s
 
 
 def test_query_rows_use_context_q_scale():
@@ -429,8 +440,12 @@ def test_query_rows_use_context_q_scale():
     qt = icl.scale_queries(x.q_ctx[0], icl.SCALE_GATED_LOG, c.k_h, x.gate_ctx[0])
     for h in range(x.workload.heads):
         a = np.max(np.abs(qt[:, h].astype(np.float64)))
-        qu, inv = icl.fp8_query_scale(a, c.scales[1, 0, h])
-        assert c.scales[0, 0, h] == qu and c.inv[0, 0, h] == inv
+        s, inv = icl.fp8_scale(a)
+        assert c.scales[0, 0, h] == s and c.inv[0, 0, h] == inv
+    # a query row far above the context's Q amax saturates at +-448 codes
+    big = np.full((1, x.workload.heads, 64), 60000, dtype=np.float16)
+    qb = icl.scale_queries(big, icl.SCALE_GATED_LOG, c.k_h, np.zeros((1, x.workload.heads), np.float16))
+    assert np.all(np.abs(c.qhat(qb, 0, 0)) == 448.0 * float(c.scales[0, 0, 0]))
     # splitting queries into batches cannot change any row
     full = icl.attend(c, x.q_query[0], x.gate_query[0], heads=[1])
     half = np.concatenate([icl.attend(c, x.q_query[0, :16], x.gate_query[0, :16], heads=[1]),
