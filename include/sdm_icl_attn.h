@@ -8,8 +8,9 @@
  * query rows attend to the context keys/values only, either in the same call
  * or later from a cached K/V ("[FP8 3/4] Integrate FP8 attention and caching
  * into TabICLv2": model(context, labels, queries), model.fit(context, labels)
- * then model.predict(queries); shared attention projects Q/K/V and falls back
- * to scaled dot-product attention).  For a query row i:
+ * then model.predict(queries); walkthrough: Q/K/V come from one shared
+ * projection and attention is scaled dot-product attention).  For a query
+ * row i:
  *
  *     O_i = sum_{j < n} softmax_j( (q~_i . k_j) / sqrt(D) ) v_j
  *
@@ -24,15 +25,18 @@
  *
  * With FP8 precision ("[FP8 3/4] ...", introduction) Q~, K and V are
  * quantised to OCP e4m3 with per-(batch, head) scales taken over the valid
- * context rows, codes = e4m3_rne(clamp(fp32(x * inv), -448, 448)).  K and V:
- * s = amax/448, inv = 448/amax.  Q (from the *scaled context* queries): the
- * smallest context-derived scale for which the logit of one unit of
- * sum_d q_code k_code is a power of two, q_unit = 2^E: with
- * base = fp32(fp32(log2(e)/sqrt(D)) * s_k), E is the smallest integer with
- * fp32(amax_q * base) <= 448 * 2^E and inv_q = base * 2^-E (E = 0 for an
- * all-zero Q); the attention kernels apply 2^E exactly as the MFMA's operand
- * scale.  Query rows reuse the context's Q scale, so a row's result does not
- * depend on how the queries are split into batches.  Softmax and
+ * context rows: s = amax/448, inv = 448/amax (amax = 0 gives 1), codes =
+ * e4m3_rne(clamp(fp32(x * inv), -448, 448)); Q's scale comes from the *scaled
+ * context* queries and query rows reuse it, so a row's result does not
+ * depend on how the queries are split into batches.  These are the scales a
+ * cache exports.  The attention kernels quantise their Q operand with a
+ * context-derived scale of their own, the one for which the logit of one
+ * unit of sum_d q_code k_code is a power of two, q_unit = 2^E (base =
+ * fp32(fp32(log2(e)/sqrt(D)) * s_k), E the smallest integer with
+ * fp32(amax_q * base) <= 448 * 2^E, inv = base * 2^-E), so that the MFMA
+ * applies the logit factor exactly as its operand scale; it is a function
+ * of (s_q, s_k) alone, and its results agree with those of the method's Q
+ * codes to within the FP8 tolerance, not bit for bit.  Softmax and
  * accumulation are fp32; outputs are fp16.
  *
  * Conventions (all entry points)
@@ -144,8 +148,11 @@ typedef struct {
 sdm_icl_status sdm_icl_attn_fit(const sdm_icl_fit_args* args, sdm_icl_cache* out);
 
 /* Device workspace (bytes) that sdm_icl_attn_query needs for n_query rows:
- * per KV split, (m, l) in fp32 and the split's normalised output row O / l in
- * fp16. */
+ * the scaled (and quantised) query operand and, per KV split, (m, l) in fp32
+ * and the split's normalised output row O / l in fp16.  The caller owns the
+ * workspace, so the query itself allocates nothing (the caller-owned-buffer
+ * rule of "... make trtllm::kda_decode inplace-only", walkthrough; the cached
+ * predict of "[FP8 3/4] ...", introduction). */
 sdm_icl_status sdm_icl_attn_query_workspace_size(sdm_icl_cache cache, int64_t n_query,
                                                  size_t* bytes);
 
@@ -174,11 +181,14 @@ sdm_icl_status sdm_icl_attn_cache_info(sdm_icl_cache cache, sdm_icl_cache_info* 
 sdm_icl_status sdm_icl_attn_cache_lengths(sdm_icl_cache cache, int64_t* host_lengths,
                                           float* host_length_scalars);
 
-/* Copy the cached operands to host memory (parity checks, persistence).
+/* Copy the cached operands to host memory, so that a fitted cache can be
+ * kept or moved to another device or process ("[FP8 3/4] ...", walkthrough:
+ * the FP8 caches survive migration and chunking).
  * host_k / host_v: [B, H, n, D] elements with n = n_valid (rows n_b..n-1 of a
  * shorter batch element are 0), 1 byte (e4m3 code) in FP8 mode or
- * 2 bytes (fp16) in FP16 mode; host_scales: float32 [3, B, H] = q_unit, s_k,
- * s_v (all 1 in FP16 mode).  Any of the three may be NULL.  Synchronises `stream`. */
+ * 2 bytes (fp16) in FP16 mode; host_scales: float32 [3, B, H] = s_q, s_k,
+ * s_v, each fp32(amax/448) (all 1 in FP16 mode).  Any of the three may be
+ * NULL.  Synchronises `stream`. */
 sdm_icl_status sdm_icl_attn_cache_export(sdm_icl_cache cache, void* host_k, void* host_v,
                                          float* host_scales, void* stream);
 
@@ -193,20 +203,19 @@ typedef struct {
   const void* host_k;         /* host [B, H, n, D], n = max n_b, as cache_export writes it:
                                  e4m3 codes (1 byte) or fp16; rows >= n_b are ignored */
   const void* host_v;         /* host [B, H, n, D], same element type */
-  const float* host_scales;   /* host float32 [3, B, H]: q_unit, s_k, s_v (all 1 for FP16) */
+  const float* host_scales;   /* host float32 [3, B, H]: s_q, s_k, s_v (all 1 for FP16) */
   void* stream;               /* hipStream_t */
 } sdm_icl_import_args;
 
 /* Rebuild a cache from what cache_export wrote (persistence, migration to
  * another device or process; the pages' FP8 caches are migrated and
  * preserved through chunking, "[FP8 3/4] ...", walkthrough).  FP8 codes and
- * scales are taken as they are; the inverse scales are recovered exactly, for
- * K and V from s = fp32(amax/448) (the amax is an fp16 value), for Q from
- * q_unit and s_k, so queries on the imported cache reproduce those on the
- * exported one bit for bit.  K/V scales not of that form and a q_unit that
- * is not a normal power of two are SDM_ICL_E_INVALID, as are e4m3 NaN codes
- * (0x7F, 0xFF).  Allocates the cache on args->stream and
- * synchronises that stream before it returns. */
+ * scales are taken as they are; from each s = fp32(amax/448) the fp16 amax
+ * is recovered exactly, and with it the inverse scales and the kernels' own
+ * Q operand scale, so queries on the imported cache reproduce those on the
+ * exported one bit for bit.  Scales not of that form are SDM_ICL_E_INVALID,
+ * as are e4m3 NaN codes (0x7F, 0xFF).  Allocates the cache on args->stream
+ * and synchronises that stream before it returns. */
 sdm_icl_status sdm_icl_attn_cache_import(const sdm_icl_import_args* args, sdm_icl_cache* out);
 
 /* Host offload ("[FP8 3/4] ...", introduction: cache chunking and CPU
@@ -225,8 +234,9 @@ sdm_icl_status sdm_icl_attn_cache_import(const sdm_icl_import_args* args, sdm_ic
 sdm_icl_status sdm_icl_attn_cache_offload(sdm_icl_cache cache, size_t chunk_bytes, void* stream);
 sdm_icl_status sdm_icl_attn_cache_restore(sdm_icl_cache cache, void* stream);
 
-/* Free a cache.  The memory is returned stream-ordered on the stream the cache
- * was fitted on; work on other streams that uses the cache must be complete
+/* Free a cache (the end of a fitted cache's life: model.fit builds it,
+ * model.predict reuses it, "[FP8 3/4] ...", introduction).  The memory is
+ * returned stream-ordered on the stream the cache was fitted on; work on other streams that uses the cache must be complete
  * (or ordered before that stream) first.  A second release of the same handle
  * returns SDM_ICL_E_STATE. */
 sdm_icl_status sdm_icl_attn_release(sdm_icl_cache cache);
@@ -247,7 +257,7 @@ sdm_icl_status sdm_icl_log_scale(const void* q, const void* gate, int32_t batch,
                                  const float* q_inv_scale, void* out, void* stream);
 
 /* The shared Q/K/V projection with the query scaling fused into its
- * epilogue ("[FP8 3/4] ...", walkthrough: shared attention projects Q/K/V;
+ * epilogue ("[FP8 3/4] ...", walkthrough: Q/K/V come from one shared projection;
  * "Fuse shared-length query scaling during inference", Solution: the scaling
  * joins the producer of q instead of separate passes over it).
  *   x:    device fp16 [B, rows, in_features] hidden rows (in_features % 32 == 0)
@@ -330,7 +340,9 @@ sdm_icl_status sdm_icl_scope_pop(void);
 /* 1 if the calling thread's effective FP8 scope setting is ENABLE, else 0. */
 int32_t sdm_icl_scope_fp8(void);
 
-/* Message of the last non-OK status on this thread ("" if none). */
+/* Message of the last non-OK status on this thread ("" if none): errors are
+ * status codes, never exceptions across the boundary, like the RuntimeError
+ * the pages raise for a misused FP8 cache ("[FP8 3/4] ...", walkthrough). */
 const char* sdm_icl_last_error(void);
 
 /* ABI version (major * 100 + minor). */

@@ -10,8 +10,9 @@
 //
 // Semantics: scaled dot-product attention of the (scaled, optionally
 // quantised) queries over the cached keys/values, as in "[FP8 3/4] Integrate
-// FP8 attention and caching into TabICLv2" (shared attention projects Q/K/V
-// and falls back to SDPA; FP8 Q/K/V with per-head scales).
+// FP8 attention and caching into TabICLv2" (walkthrough: the attention is
+// PyTorch's scaled dot-product attention; introduction: FP8 Q/K/V with
+// per-head scales).
 //
 // Data flow of one workgroup (W = 2 or 4 wavefronts, each owning QG x 32
 // query rows; a wavefront walks its whole KV range, so the block shape does
@@ -24,8 +25,9 @@
 //     32x32x16_f16.  K rows are fed in a permuted order so that each lane
 //     ends up holding, for its own query, exactly the 8-key groups that the
 //     PV MFMA wants in its B operand: P never leaves registers.
-//   * Online softmax in base 2.  FP8: the logit factor is a power of two
-//     (the cache's q_unit = 2^E) that the MFMA applies as its E8M0 operand
+//   * Online softmax in base 2.  FP8: the Q operand is quantised with a
+//     context-derived scale for which the logit factor is a power of two
+//     (the cache's q_unit = 2^E), which the MFMA applies as its E8M0 operand
 //     scale, and after the first tile the MFMA accumulates onto -m, so it
 //     returns the shifted logit and P = exp2 of it.  FP16: the scale and the
 //     reference are folded into one FMA per score.
@@ -293,13 +295,25 @@ __device__ __forceinline__ void attend_tile(WaveState<PREC, QG>& w, const unsign
         for (int c = 0; c < 2; ++c) s[c] = chunk_scores<PREC, MASK>(kb, c, col, hf, w.qf[g], rem, lg);
         const float mt = tile_max(s) * c_scale;
         const float mnew = over ? fmaxf(w.m_run[g], mt) : w.m_run[g];
-        const float alpha = __builtin_amdgcn_exp2f(w.m_run[g] - mnew);
+        const float alpha = __builtin_amdgcn_exp2f(w.m_run[g] - mnew);  // exactly 1 unless over
         w.m_run[g] = mnew;
         if constexpr (PREC == kPrecFp8) w.neg_m[g] = -mnew;
         w.l_run[g] *= alpha;
         w.o[g][0] *= alpha;
         w.o[g][1] *= alpha;
-        lt[g] = exp_chunk(s[0], c_scale, -mnew, p16[g][0]) + exp_chunk(s[1], c_scale, -mnew, p16[g][1]);
+        f16x8 pn[2][2];
+        const float ln = exp_chunk(s[0], c_scale, -mnew, pn[0]) + exp_chunk(s[1], c_scale, -mnew, pn[1]);
+        // Rows that did not overflow keep the P (and its sum) of the normal
+        // path: for FP8 that P came from an MFMA started at -m, which can
+        // round differently from exp2(s - m) here, and a row's bits must not
+        // depend on whether a neighbour in its group moved its reference.
+        if (over) {
+          lt[g] = ln;
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) p16[g][c][ks] = pn[c][ks];
+        }
       }
     }
 #pragma unroll
@@ -392,13 +406,13 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
     return;
   }
 
-  // logit (log2 units) = raw dot * lg.c (FP16); FP8: the Q slot of the
-  // scales holds q_unit = 2^E, whose exponent field is the E8M0 operand scale
-  // that makes the MFMA return the logit itself
+  // logit (log2 units) = raw dot * lg.c (FP16); FP8: the exponent field of
+  // q_unit = 2^E is the E8M0 operand scale that makes the MFMA return the
+  // logit itself
   Logit lg = {a.tau_log2e, 127};
   float sv = 1.0f;
   if constexpr (PREC == kPrecFp8) {
-    lg = {1.0f, (int)((__float_as_uint(a.scales[bh]) >> 23) & 0xFF)};
+    lg = {1.0f, (int)((__float_as_uint(a.q_unit[bh]) >> 23) & 0xFF)};
     sv = a.scales[2 * a.bh_count + bh];
   }
 

@@ -7,7 +7,7 @@
 // then V), accumulation in float32 and one rounding to fp16; the Q columns
 // then take LogScale / GatedLogScale exactly as the separate scaling pass does
 // ("[FP8 3/4] Integrate FP8 attention and caching into TabICLv2", walkthrough:
-// shared attention projects Q/K/V; "Fuse shared-length query scaling during
+// Q/K/V come from one shared projection; "Fuse shared-length query scaling during
 // inference", Solution: the scaling is fused into the producer of q, with the
 // float32 length arithmetic and fp16 rounding boundaries of the eager path).
 //

@@ -287,32 +287,33 @@ def test_import_validates_before_touching_the_device():
 
 
 def test_import_accepts_the_scale_of_every_fp16_amax():
-    """fit writes s = fp32(a/448) for an fp16 amax a; import must recognise
-    every such s (it recovers a, and with it the exact inverse scale)."""
+    """fit writes s = fp32(a/448) for an fp16 amax a, for Q, K and V alike;
+    import must recognise every such s (it recovers a, and with it the exact
+    inverse scale and the kernels' Q operand scale)."""
     k = np.zeros((1, 1, 1, 64), dtype=np.uint8)
     a = _all_finite_fp16_positive()
     bad = []
     for i in range(a.size):
         s = icl.fp8_scale(a[i])[0]
         sc = np.full((3, 1, 1), s, dtype=np.float32)
-        sc[0] = 1.0                      # the Q slot holds q_unit, a power of two
         if _import_status(k, k, sc, lengths=(1,)) == 1:
             bad.append(float(a[i]))
     assert not bad, bad[:5]
 
 
-def test_import_requires_a_power_of_two_query_unit():
-    """The Q slot of FP8 scales is q_unit = 2^E (the logit of one unit of the
-    code dot product); anything else is rejected before the device."""
+def test_import_rejects_a_query_scale_that_is_no_amax_scale():
+    """The Q slot holds s_q = fp32(amax/448) like K and V: 1.0 (an all-zero
+    or 448 amax) and every fp16 amax's quotient pass; other values are
+    rejected before the device."""
     k = np.zeros((1, 1, 1, 64), dtype=np.uint8)
     passed = lambda st: st not in (1, 2)
-    for qu in (2.0 ** -60, 2.0 ** -17, 0.5, 1.0, 8.0):
-        sc = np.array([[[qu]], [[0.25]], [[0.25]]], dtype=np.float32)
+    for qs in (1.0, float(icl.fp8_scale(0.125)[0]), float(icl.fp8_scale(2.5)[0])):
+        sc = np.array([[[qs]], [[0.25]], [[0.25]]], dtype=np.float32)
         assert passed(_import_status(k, k, sc, lengths=(1,)))
-    for qu in (0.3, 3.0, -0.5, 0.0, np.inf, np.nan, 2.0 ** -140):
-        sc = np.array([[[qu]], [[0.25]], [[0.25]]], dtype=np.float32)
+    for qs in (0.3, 3.01, -0.5, 0.0, np.inf, np.nan):
+        sc = np.array([[[qs]], [[0.25]], [[0.25]]], dtype=np.float32)
         assert _import_status(k, k, sc, lengths=(1,)) == 1
-        assert "power of two" in B.sdm_icl_last_error()
+        assert "scale" in B.sdm_icl_last_error()
 
 
 def _all_finite_fp16_positive():
