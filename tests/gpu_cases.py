@@ -8,7 +8,9 @@ all-zero output).  Bounds: 2e-3 for FP16, 2e-2 for FP8.
 """
 from __future__ import annotations
 
+import os
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -79,9 +81,60 @@ class Run:
 
     def ref_context(self, rows, heads=None, b: int = 0) -> np.ndarray:
         gate = self.x.gate_ctx if self.gate is not None else None
-        return icl.context_outputs(self.oracle, self.x.q_ctx, gate, rows, b=b, heads=heads)
+        return parallel_rows(lambda r, h: icl.context_outputs(self.oracle, self.x.q_ctx, gate, r, b=b,
+                                                               heads=h),
+                             rows, self.w.heads if heads is None else heads)
 
     def ref_query(self, rows, heads=None, b: int = 0) -> np.ndarray:
         rows = np.asarray(rows)
-        gate = self.x.gate_query[b, rows] if self.gq is not None else None
-        return icl.attend(self.oracle, self.x.q_query[b, rows], gate, b=b, heads=heads)
+        gate_all = self.x.gate_query[b] if self.gq is not None else None
+
+        def one(r, h):
+            g = None if gate_all is None else gate_all[r]
+            return icl.attend(self.oracle, self.x.q_query[b, r], g, b=b, heads=h)
+        return parallel_rows(one, rows, self.w.heads if heads is None else heads)
+
+
+def parallel_rows(fn, rows, heads) -> np.ndarray:
+    """Evaluate the oracle over (row block, head) pieces in a thread pool.
+
+    ``fn(rows, [h])`` is an oracle call that returns float64 ``[len(rows), H,
+    D]`` with head h filled.  Each piece is the oracle's own computation on a
+    subset (rows and heads are independent in attention), so the result is
+    the same as one call; numpy releases the GIL inside its array operations,
+    so the pieces run on the host's cores.  BLAS is held to one thread per
+    piece; each piece is one head and a share of the rows, so that it decodes
+    that head's keys once.
+    """
+    rows = np.asarray(rows, dtype=np.int64)
+    heads = list(heads) if not isinstance(heads, int) else list(range(heads))
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    groups = max(1, -(-workers // len(heads)))
+    block = max(1, -(-rows.size // groups))
+    pieces = [(r0, h) for h in heads for r0 in range(0, rows.size, block)]
+    parts = {}
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+
+    def run(piece):
+        r0, h = piece
+        parts[piece] = fn(rows[r0:r0 + block], [h])
+
+    workers = min(workers, len(pieces))
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            with ThreadPoolExecutor(max_workers=workers) as pool:
+                list(pool.map(run, pieces))
+    else:  # pragma: no cover
+        with ThreadPoolExecutor(max_workers=workers) as pool:
+            list(pool.map(run, pieces))
+    out = None
+    for (r0, h), part in parts.items():
+        if out is None:
+            out = np.zeros((rows.size,) + part.shape[1:], dtype=np.float64)
+        out[r0:r0 + block, h] = part[:, h]
+    if out is None:
+        out = np.zeros((0, 0, 0))
+    return out

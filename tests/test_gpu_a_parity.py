@@ -291,11 +291,70 @@ def test_reference_moves_when_later_tiles_dominate(prec):
     assert e_c <= TOL[prec] and e_q <= TOL[prec]
 
 
+@pytest.mark.parametrize("prec", [B.SDM_ICL_PREC_FP16, B.SDM_ICL_PREC_FP8_E4M3])
+def test_rows_beside_a_moving_reference_keep_their_bits(prec):
+    """Only query rows 0..9 meet a key far above their first-tile reference
+    (they point at key 1,500), so they move it; rows 10.. have logits with a
+    spread of a few log2 units that never overflow.  Split at rows 10 and 20
+    (not multiples of the 32-row groups), rows 10..31 share a group with the
+    moving rows in one launch and not in the other: their bits must not
+    change."""
+    torch = _torch()
+    rng = np.random.default_rng(23)
+    N, H, R = 2048, 2, 96
+    k = (rng.standard_normal((1, N, H, 64)) / 8).astype(np.float16)
+    v = (rng.standard_normal((1, N, H, 64)) / 8).astype(np.float16)
+    qq = (rng.standard_normal((1, R, H, 64)) * 16).astype(np.float16)
+    target = k[0, 1500].astype(np.float64)
+    qq[0, :10] = (200.0 * target / np.linalg.norm(target, axis=-1, keepdims=True)).astype(np.float16)
+    q = (rng.standard_normal((1, N, H, 64)) * 16).astype(np.float16)
+    q[0, 0, :, 0] = 250                              # context Q amax above every query element
+    say("rows beside a moving reference", prec)
+    c = B.sdm_icl_attn_fit(to_dev(q), to_dev(k), to_dev(v), N, precision=prec)
+    full = B.sdm_icl_attn_query(c, to_dev(qq)).cpu().numpy()
+    for cut in (10, 20):
+        parts = np.concatenate([B.sdm_icl_attn_query(c, to_dev(qq[:, :cut])).cpu().numpy(),
+                                B.sdm_icl_attn_query(c, to_dev(qq[:, cut:])).cpu().numpy()], axis=1)
+        np.testing.assert_array_equal(full.view(np.uint16), parts.view(np.uint16))
+    torch.cuda.synchronize()
+    c.release()
+    ref = icl.fit(q, k, v, N, icl.SCALE_NONE, prec)
+    e_q = norm_err(full[0].astype(np.float64), icl.attend(ref, qq[0], None))
+    say(f"  query err {e_q:.3e}")
+    assert e_q <= TOL[prec]
+
+
+def test_fp8_query_rows_above_the_context_amax_saturate():
+    """Query rows reuse the context's Q scale: elements beyond the context
+    amax saturate at it (the method's +-448 codes).  Queries drawn 32x wider
+    than the context's Q saturate in most elements; the result follows the
+    oracle's saturated rows."""
+    torch = _torch()
+    rng = np.random.default_rng(29)
+    N, H, R = 1500, 2, 100
+    q = (rng.standard_normal((1, N, H, 64)) / 8).astype(np.float16)
+    k = (rng.standard_normal((1, N, H, 64)) / 8).astype(np.float16)
+    v = (rng.standard_normal((1, N, H, 64)) / 8).astype(np.float16)
+    qq = (rng.standard_normal((1, R, H, 64)) * 4).astype(np.float16)
+    say("fp8 query saturation")
+    c = B.sdm_icl_attn_fit(to_dev(q), to_dev(k), to_dev(v), N, precision=B.SDM_ICL_PREC_FP8_E4M3)
+    got = B.sdm_icl_attn_query(c, to_dev(qq)).cpu().numpy()[0].astype(np.float64)
+    torch.cuda.synchronize()
+    c.release()
+    ref = icl.fit(q, k, v, N, icl.SCALE_NONE, icl.PREC_FP8_E4M3)
+    frac = np.mean(np.abs(qq[0].astype(np.float64)) > icl.amax_rows(q[0])[None, :, None])
+    want = icl.attend(ref, qq[0], None)
+    err = norm_err(got, want)
+    say(f"  saturated fraction {frac:.2f}, normalised error {err:.2e}")
+    assert frac > 0.5
+    assert err <= TOL[B.SDM_ICL_PREC_FP8_E4M3]
+
+
 def test_fp8_query_scale_edges():
-    """The power-of-two Q unit at its edges: an all-zero Q (E = 0; every key
-    equally weighted, so each row returns the mean of the dequantised V) and
-    large-magnitude queries against tiny keys (E far from 0), each against
-    the oracle."""
+    """The kernels' own Q operand scale (power-of-two logit unit) at its
+    edges: an all-zero Q (every key equally weighted, so each row returns the
+    mean of the dequantised V) and large-magnitude queries against tiny keys
+    (E far from 0), each against the oracle's plain per-head Q scale."""
     torch = _torch()
     rng = np.random.default_rng(71)
     N, H = 300, 2
@@ -318,9 +377,67 @@ def test_fp8_query_scale_edges():
         want = icl.context_outputs(ref, q, None, rows)
         got = out.cpu().numpy()[0].astype(np.float64)
         err = norm_err(got, want)
-        say(f"  normalised error {err:.2e}, q_unit {sc[0, 0, 0]!r}")
+        say(f"  normalised error {err:.2e}, s_q {sc[0, 0, 0]!r}")
         assert err <= TOL[B.SDM_ICL_PREC_FP8_E4M3]
         if name == "zero q":
             assert sc[0, 0, 0] == 1.0
             mean_v = np.stack([ref.vhat(0, h).mean(axis=0) for h in range(H)])
             np.testing.assert_allclose(got, np.broadcast_to(mean_v, got.shape), rtol=0, atol=2e-3 * np.abs(mean_v).max())
+
+
+def test_fp8_path_equals_fp16_path_on_grid_inputs():
+    """I10 on the GPU: Q~, K and V drawn from the e4m3 grid times a
+    power-of-two scale per tensor and head (amax pinned to 448 s), so the
+    method's FP8 quantisation is lossless: the oracle's FP8 and FP16 results
+    are identical, and the kernels' K/V codes and the exported scales must be
+    exactly the grid's.  The kernels' own Q operand scale requantises Q, and
+    P is rounded to fp16, so the GPU's FP8 path must match its FP16 path
+    (and the oracle) within the FP8 tolerance.  One head has tiny logits,
+    the other a spread of about 0.8."""
+    torch = _torch()
+    rng = np.random.default_rng(31)
+    N, H, R = 640, 2, 96
+    grid = numerics.E4M3_VALUES[np.isfinite(numerics.E4M3_VALUES)]
+    grid = grid[np.abs(grid) <= 64]
+    scales = {"q": (2.0 ** -9, 2.0 ** -3), "k": (2.0 ** -10, 2.0 ** -5), "v": (2.0 ** -6, 2.0 ** -11)}
+    amax_dim = {"q": 0, "k": 1, "v": 2}     # the pinned amax elements never meet in a dot product
+
+    def draw(name, rows):
+        t = np.empty((1, rows, H, 64))
+        for h in range(H):
+            t[0, :, h] = rng.choice(grid, size=(rows, 64)) * scales[name][h]
+            t[0, 0, h, amax_dim[name]] = 448 * scales[name][h]
+        assert np.all(t.astype(np.float16).astype(np.float64) == t)
+        return t.astype(np.float16)
+
+    q, k, v = draw("q", N), draw("k", N), draw("v", N)
+    qq = draw("q", R)
+    qq[0, 0] = qq[0, 1]                     # query rows stay within the context amax
+    say("I10 grid inputs")
+    outs = {}
+    for prec in (B.SDM_ICL_PREC_FP16, B.SDM_ICL_PREC_FP8_E4M3):
+        out = torch.empty((1, N, H, 64), dtype=torch.float16, device="cuda")
+        c = B.sdm_icl_attn_fit(to_dev(q), to_dev(k), to_dev(v), N, precision=prec, out_ctx=out)
+        oq = B.sdm_icl_attn_query(c, to_dev(qq))
+        if prec == B.SDM_ICL_PREC_FP8_E4M3:
+            kc, vc, sc = B.sdm_icl_attn_cache_export(c)
+        torch.cuda.synchronize()
+        c.release()
+        outs[prec] = (out.cpu().numpy()[0].astype(np.float64), oq.cpu().numpy()[0].astype(np.float64))
+    ref8 = icl.fit(q, k, v, N, icl.SCALE_NONE, icl.PREC_FP8_E4M3)
+    ref16 = icl.fit(q, k, v, N, icl.SCALE_NONE, icl.PREC_FP16)
+    for t, name in enumerate("qkv"):
+        np.testing.assert_array_equal(sc[t, 0], np.float32(scales[name]))
+    np.testing.assert_array_equal(kc, ref8.k_codes)
+    np.testing.assert_array_equal(vc, ref8.v_codes)
+    for which, rows_q in ((0, q[0]), (1, qq[0])):
+        want = icl.attend(ref16, rows_q, None)
+        assert np.array_equal(icl.attend(ref8, rows_q, None), want)
+        o16, o8 = outs[B.SDM_ICL_PREC_FP16][which], outs[B.SDM_ICL_PREC_FP8_E4M3][which]
+        for h in range(H):
+            e_paths = norm_err(o8[:, h], o16[:, h])
+            e8, e16 = norm_err(o8[:, h], want[:, h]), norm_err(o16[:, h], want[:, h])
+            say(f"  {'context' if which == 0 else 'query'} head {h}: FP8 vs FP16 path {e_paths:.2e}, "
+                f"FP8 vs oracle {e8:.2e}, FP16 vs oracle {e16:.2e}")
+            assert e_paths <= TOL[B.SDM_ICL_PREC_FP8_E4M3] and e8 <= TOL[B.SDM_ICL_PREC_FP8_E4M3]
+            assert e16 <= TOL[B.SDM_ICL_PREC_FP16]

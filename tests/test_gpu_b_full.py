@@ -1,7 +1,11 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
-benchmark uses.  Outputs are compared with the float64 oracle on seeded
-samples of rows (each against all n keys), FP8 codes and scales bitwise, and
-the bitwise invariants at full size."""
+benchmark uses.  Outputs are compared element by element with the float64
+oracle (each row against all n keys): every row of the tiny and the 16K
+workloads, every query row of the others, and seeded samples of context rows
+(2,048 at 128K; 1,024 valid rows, including the first and last 8, at 512K);
+FP8 codes and scales bitwise; and the bitwise invariants at full size.  The
+oracle runs on the host's cores, one head and a share of the rows per
+thread."""
 import numpy as np
 import pytest
 
@@ -26,7 +30,7 @@ def _check(run, out_ctx, out_q, ctx_rows, q_rows):
     assert e_c <= tol and e_q <= tol
 
 
-@pytest.mark.timeout(300)
+@pytest.mark.timeout(600)
 def test_full_tiny_fp16():
     import torch
     r = Run(gen.WORKLOADS["tiny_fp16"])
@@ -38,7 +42,7 @@ def test_full_tiny_fp16():
     _check(r, out.cpu().numpy(), oq.cpu().numpy(), np.arange(1024), np.arange(64))
 
 
-@pytest.mark.timeout(300)
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["ctx16k_log_fp16", "ctx16k_gated_fp16"])
 def test_full_ctx16k(name):
     import torch
@@ -48,10 +52,10 @@ def test_full_ctx16k(name):
     oq = r.query(cache)
     torch.cuda.synchronize()
     cache.release()
-    _check(r, out.cpu().numpy(), oq.cpu().numpy(), gen.sample_rows(16384, 256, 1), np.arange(0, 1024, 8))
+    _check(r, out.cpu().numpy(), oq.cpu().numpy(), np.arange(16384), np.arange(1024))
 
 
-@pytest.mark.timeout(300)
+@pytest.mark.timeout(600)
 def test_full_ctx128k_fp8():
     import torch
     r = Run(gen.WORKLOADS["ctx128k_fp8"])
@@ -65,10 +69,10 @@ def test_full_ctx128k_fp8():
     np.testing.assert_array_equal(sc, o.scales)
     np.testing.assert_array_equal(k, o.k_codes)
     np.testing.assert_array_equal(v, o.v_codes)
-    _check(r, out.cpu().numpy(), oq.cpu().numpy(), gen.sample_rows(131072, 64, 2), np.arange(0, 1024, 16))
+    _check(r, out.cpu().numpy(), oq.cpu().numpy(), gen.sample_rows(131072, 2048, 2), np.arange(1024))
 
 
-@pytest.mark.timeout(300)
+@pytest.mark.timeout(600)
 def test_full_cached512k_fp8_gated():
     """Cached prediction against a resident 524,288-row FP8 cache: sampled
     parity, and 8 x 128 query batches bit-identical to 1 x 1,024."""
@@ -93,11 +97,10 @@ def test_full_cached512k_fp8_gated():
     np.testing.assert_array_equal(full.view(np.uint16), streamed.view(np.uint16))
     np.testing.assert_array_equal(full[:, 384:512].view(np.uint16), streamed128.view(np.uint16))
     np.testing.assert_array_equal(sc, r.oracle.scales)
-    rows = np.concatenate([np.arange(4), np.arange(1020, 1024), np.arange(127, 1024, 113)])
-    _check(r, None, full, [], np.unique(rows))
+    _check(r, None, full, [], np.arange(1024))
 
 
-@pytest.mark.timeout(300)
+@pytest.mark.timeout(600)
 def test_full_model512k_fp8_log():
     """Full model call at 524,288 padded rows (last 1,000 masked, NaN-filled)."""
     import torch
@@ -112,10 +115,10 @@ def test_full_model512k_fp8_log():
     out = out.cpu().numpy()
     assert info["n_valid"] == 523288 and info["length_scalar"] == r.oracle.L32
     assert np.all(out[0, w.n_valid:] == 0)
-    _check(r, out, oq.cpu().numpy(), gen.sample_rows(w.n_valid, 24, w.seed), np.arange(0, 1024, 64))
+    _check(r, out, oq.cpu().numpy(), gen.sample_rows(w.n_valid, 1024, w.seed), np.arange(1024))
 
 
-@pytest.mark.timeout(300)
+@pytest.mark.timeout(600)
 def test_full_ragged_two_contexts_in_one_cache():
     """Two batch elements with 524,288 and 300,001 valid rows in one fit and
     one query launch (per-batch lengths, FP8, GatedLogScale, outliers, NaN
