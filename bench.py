@@ -30,6 +30,10 @@ if ROOT not in sys.path:
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA
 PEAK_FP16_TFLOPS = 2500.0    # MI355X dense FP16 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+# The FP8 attention kernels run QK^T on the FP8 pipe and PV on the FP16 pipe
+# (P is fp16): half of the 4 n^2 D H FLOP at each peak, so the MFMA ceiling of
+# that mix is 4 / (2 / 5000 + 2 / 2500) = 3333.3 TFLOP/s.
+PEAK_MIXED_TFLOPS = 4.0 / (2.0 / PEAK_FP8_TFLOPS + 2.0 / PEAK_FP16_TFLOPS)
 
 
 def log(*a):
@@ -186,6 +190,32 @@ def bench_model_call(B, gen, w, steps, warmup):
                 ("prep", B.SDM_ICL_TIMING_PREP))}
     B.sdm_icl_timing_enable(False)
     return x, info, (t1 - t0) / steps, timings
+
+
+def bench_other_workload(B, gen, name, steps, warm_ms=60.0):
+    """A model call of another workload (the 128K FP8 and the 16K FP16 ones):
+    warm-up calls adding up to about warm_ms of GPU work first (a few
+    milliseconds leave the clocks below their steady state), then `steps`
+    timed calls; the context kernel's time from the in-stream events."""
+    import math
+    w = gen.WORKLOADS[name]
+    _, info, sec1, _ = bench_model_call(B, gen, w, 1, 1)
+    warm = max(3, int(math.ceil(warm_ms / max(sec1 * 1e3, 1e-3))))
+    _, info, sec, t = bench_model_call(B, gen, w, steps, warm)
+    n, H, D, R = w.n_valid, w.heads, w.head_dim, w.n_query
+    ctx_flops = 4.0 * n * n * D * H
+    ctx_ms = t["context"][0] / max(t["context"][1], 1)
+    achieved = ctx_flops / (ctx_ms * 1e-3) / 1e12
+    fp8 = info["precision"] == 1
+    peak = PEAK_FP8_TFLOPS if fp8 else PEAK_FP16_TFLOPS
+    mixed = PEAK_MIXED_TFLOPS if fp8 else PEAK_FP16_TFLOPS
+    return {"n_valid": n, "n_query": R, "heads": H, "precision": "fp8_e4m3" if fp8 else "fp16",
+            "scale": ["none", "log", "gated_log"][w.scale_mode], "warmup": warm, "steps": steps,
+            "ms_per_step": round(sec * 1e3, 4),
+            "TFLOP_per_s_step": round((ctx_flops + 4.0 * R * n * D * H) / sec / 1e12, 1),
+            "context_kernel_ms": round(ctx_ms, 4), "context_TFLOP_per_s": round(achieved, 1),
+            "peak": peak, "frac": round(achieved / peak, 4),
+            "peak_mixed": round(mixed, 1), "frac_mixed": round(achieved / mixed, 4)}
 
 
 def bench_cached(B, gen, w, reps, offload=True, warmup=300):
@@ -376,6 +406,9 @@ def main() -> int:
                     help="skip the model-call measurement (only the cached-prediction leg runs)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip measuring the sustained MFMA and HBM-read peaks")
+    ap.add_argument("--no-other", action="store_true",
+                    help="skip the 128K FP8 and 16K FP16 model calls")
+    ap.add_argument("--other-workloads", default="ctx128k_fp8,ctx16k_log_fp16,ctx16k_gated_fp16")
     ap.add_argument("--cpu-sample-rows", type=int, default=384)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times) and exit; "
@@ -424,6 +457,7 @@ def main() -> int:
     achieved = ctx_flops / (ctx_avg * 1e-3) / 1e12
     prec_name = "fp8_e4m3" if info["precision"] == 1 else "fp16"
     peak = PEAK_FP8_TFLOPS if info["precision"] == 1 else PEAK_FP16_TFLOPS
+    peak_mixed = PEAK_MIXED_TFLOPS if info["precision"] == 1 else PEAK_FP16_TFLOPS
     log(f"[bench] step {sec * 1e3:.2f} ms, {value:.1f} TFLOP/s; context kernel {ctx_avg:.3f} ms "
         f"({achieved:.1f} TFLOP/s)")
     line = {
@@ -446,6 +480,8 @@ def main() -> int:
         "roofline": {"bound": "mfma", "kernel": "attention_kernel (context pass)",
                      "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4),
+                     # the MFMA ceiling of FP8 QK^T + FP16 PV (see PEAK_MIXED_TFLOPS)
+                     "peak_mixed": round(peak_mixed, 1), "frac_mixed": round(achieved / peak_mixed, 4),
                      # the committed counter record is for the 512K model call only
                      "traffic": counter_traffic("context") if w.name == "model512k_fp8_log" else None,
                      "launch_ms": round(ctx_avg, 4), "launches": ctx_n},
@@ -474,6 +510,12 @@ def main() -> int:
         if peaks and r128:
             line["cached"]["hbm_frac_of_measured"] = round(r128["GB_per_s"] / peaks["hbm_read_GB_per_s_4GiB"], 4)
         log(f"[bench] cached: {json.dumps(line['cached'])}")
+    if not args.no_other:
+        line["other_workloads"] = {}
+        for name in [s for s in args.other_workloads.split(",") if s]:
+            log(f"[bench] model call {name}")
+            line["other_workloads"][name] = bench_other_workload(B, gen, name, 20 if "16k" in name else 8)
+            log(f"[bench] {name}: {json.dumps(line['other_workloads'][name])}")
     if not args.no_projection:
         line["projection"] = bench_projection(B, w)
         if peaks:
