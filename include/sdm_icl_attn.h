@@ -26,18 +26,11 @@
  * With FP8 precision ("[FP8 3/4] ...", introduction) Q~, K and V are
  * quantised to OCP e4m3 with per-(batch, head) scales taken over the valid
  * context rows: s = amax/448, inv = 448/amax (amax = 0 gives 1), codes =
- * e4m3_rne(clamp(fp32(x * inv), -448, 448)); Q's scale comes from the *scaled
- * context* queries and query rows reuse it, so a row's result does not
- * depend on how the queries are split into batches.  These are the scales a
- * cache exports.  The attention kernels quantise their Q operand with a
- * context-derived scale of their own, the one for which the logit of one
- * unit of sum_d q_code k_code is a power of two, q_unit = 2^E (base =
- * fp32(fp32(log2(e)/sqrt(D)) * s_k), E the smallest integer with
- * fp32(amax_q * base) <= 448 * 2^E, inv = base * 2^-E), so that the MFMA
- * applies the logit factor exactly as its operand scale; it is a function
- * of (s_q, s_k) alone, and its results agree with those of the method's Q
- * codes to within the FP8 tolerance, not bit for bit.  Softmax and
- * accumulation are fp32; outputs are fp16.
+ * e4m3_rne(clamp(fp32(x * inv), -448, 448)), dequantised as code * s.  Q's
+ * scale comes from the *scaled context* queries and query rows reuse it (and
+ * saturate above it), so a row's result does not depend on how the queries
+ * are split into batches.  Softmax and accumulation are fp32; outputs are
+ * fp16.
  *
  * Conventions (all entry points)
  * ------------------------------
@@ -210,12 +203,12 @@ typedef struct {
 /* Rebuild a cache from what cache_export wrote (persistence, migration to
  * another device or process; the pages' FP8 caches are migrated and
  * preserved through chunking, "[FP8 3/4] ...", walkthrough).  FP8 codes and
- * scales are taken as they are; from each s = fp32(amax/448) the fp16 amax
- * is recovered exactly, and with it the inverse scales and the kernels' own
- * Q operand scale, so queries on the imported cache reproduce those on the
- * exported one bit for bit.  Scales not of that form are SDM_ICL_E_INVALID,
- * as are e4m3 NaN codes (0x7F, 0xFF).  Allocates the cache on args->stream
- * and synchronises that stream before it returns. */
+ * scales are taken as they are; from each s = fp32(amax/448) the fp16 amax,
+ * and with it the exact inverse scale, is recovered, so queries on the
+ * imported cache reproduce those on the exported one bit for bit.  Scales
+ * not of that form are SDM_ICL_E_INVALID, as are e4m3 NaN codes (0x7F,
+ * 0xFF).  Allocates the cache on args->stream and synchronises that stream
+ * before it returns. */
 sdm_icl_status sdm_icl_attn_cache_import(const sdm_icl_import_args* args, sdm_icl_cache* out);
 
 /* Host offload ("[FP8 3/4] ...", introduction: cache chunking and CPU

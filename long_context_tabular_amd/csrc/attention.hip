@@ -25,12 +25,9 @@
 //     32x32x16_f16.  K rows are fed in a permuted order so that each lane
 //     ends up holding, for its own query, exactly the 8-key groups that the
 //     PV MFMA wants in its B operand: P never leaves registers.
-//   * Online softmax in base 2.  FP8: the Q operand is quantised with a
-//     context-derived scale for which the logit factor is a power of two
-//     (the cache's q_unit = 2^E), which the MFMA applies as its E8M0 operand
-//     scale, and after the first tile the MFMA accumulates onto -m, so it
-//     returns the shifted logit and P = exp2 of it.  FP16: the scale and the
-//     reference are folded into one FMA per score.
+//   * Online softmax in base 2: the logit factor (log2(e)/sqrt(D), times
+//     s_q s_k for FP8, whose MFMA sums code products) and the reference are
+//     folded into one FMA per score before exp2.
 //     The first tile of a wave's KV range sets each row's reference maximum;
 //     later tiles compute P against it with no per-tile max at all, and a row
 //     moves its reference (rescaling O and l) only when the 32 rounded P one
@@ -97,14 +94,12 @@ struct Ops<kPrecFp8> {
   __device__ static QFrag load_q(const unsigned char* rowp, int hf) {
     return *reinterpret_cast<const i32x8*>(rowp + 32 * hf);
   }
-  // c + 2^E * (K rows . Q): the Q operand carries the E8M0 scale q_unit8 =
-  // 127 + E, so the result is the logit in log2 units (plus c)
-  __device__ static f32x16 qk(const unsigned char* krow, int hf, const QFrag& q, const f32x16& c,
-                              int q_unit8) {
+  // c + K rows . Q on the code values (unit E8M0 operand scales)
+  __device__ static f32x16 qk(const unsigned char* krow, int hf, const QFrag& q, const f32x16& c) {
     const i32x4 a0 = *reinterpret_cast<const i32x4*>(krow + 32 * hf);
     const i32x4 a1 = *reinterpret_cast<const i32x4*>(krow + 32 * hf + 16);
     const i32x8 a = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, q, c, 0, 0, 0, 127, 0, q_unit8);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, q, c, 0, 0, 0, 127, 0, 127);
   }
 };
 
@@ -119,7 +114,7 @@ struct Ops<kPrecFp16> {
     for (int t = 0; t < 4; ++t) f.v[t] = *reinterpret_cast<const f16x8*>(rowp + 32 * t + 16 * hf);
     return f;
   }
-  __device__ static f32x16 qk(const unsigned char* krow, int hf, const QFrag& q, const f32x16& c, int) {
+  __device__ static f32x16 qk(const unsigned char* krow, int hf, const QFrag& q, const f32x16& c) {
     f32x16 acc = c;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -144,7 +139,6 @@ struct WaveState {
   typename Ops<PREC>::QFrag qf[QG];
   float m_run[QG], l_run[QG];
   f32x16 o[QG][2];
-  f32x16 neg_m[QG];  // FP8: -m_run splatted, the QK MFMA's accumulator input
 };
 
 __device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
@@ -190,31 +184,19 @@ __device__ __forceinline__ float exp_chunk(const f32x16& s, float c_scale, float
   return sum_p(p16);
 }
 
-// How a raw score becomes a logit in log2 units: FP16 multiplies by c
-// (log2(e)/sqrt(D)); FP8 gets the whole factor from the MFMA's operand scale
-// (q_unit8, an E8M0 exponent) and has c = 1.
+// How a raw score becomes a logit in log2 units: multiplied by c, which is
+// log2(e)/sqrt(D) for FP16 and log2(e)/sqrt(D) * s_q * s_k for FP8 (the
+// scores are then sums of code products).
 struct Logit {
   float c;
-  int q_unit8;
 };
-
-// P = fp16(exp2(x)) for logits x already shifted by the reference (FP8:
-// the MFMA accumulates onto -m); same rounding of P and l as exp_chunk.
-__device__ __forceinline__ float exp_chunk_shifted(const f32x16& x, f16x8 (&p16)[2]) {
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) p16[ks][e] = (_Float16)__builtin_amdgcn_exp2f(x[8 * ks + e]);
-  return sum_p(p16);
-}
 
 // Scores of one 32-key chunk, starting from the accumulator value init, with
 // keys >= n set to -inf (MASK only).
 template <int PREC, bool MASK>
 __device__ __forceinline__ f32x16 chunk_scores(const unsigned char* kb, int c, int col, int hf,
-                                               const typename Ops<PREC>::QFrag& q, int rem, Logit lg,
-                                               const f32x16& init = f32x16{}) {
-  f32x16 sc = Ops<PREC>::qk(kb + (32 * c + col) * Ops<PREC>::KROW, hf, q, init, lg.q_unit8);
+                                               const typename Ops<PREC>::QFrag& q, int rem) {
+  f32x16 sc = Ops<PREC>::qk(kb + (32 * c + col) * Ops<PREC>::KROW, hf, q, f32x16{});
   if constexpr (MASK) {
     const int lim = rem - 8 * hf;  // key offset in the tile = 32c + 16(r/8) + 8hf + r%8
 #pragma unroll
@@ -246,9 +228,8 @@ __device__ __forceinline__ void attend_tile(WaveState<PREC, QG>& w, const unsign
     for (int g = 0; g < QG; ++g) {
       f32x16 s[2];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) s[c] = chunk_scores<PREC, MASK>(kb, c, col, hf, w.qf[g], rem, lg);
+      for (int c = 0; c < 2; ++c) s[c] = chunk_scores<PREC, MASK>(kb, c, col, hf, w.qf[g], rem);
       w.m_run[g] = tile_max(s) * c_scale;
-      if constexpr (PREC == kPrecFp8) w.neg_m[g] = -w.m_run[g];
       w.l_run[g] = exp_chunk(s[0], c_scale, -w.m_run[g], p16[g][0]) +
                    exp_chunk(s[1], c_scale, -w.m_run[g], p16[g][1]);
     }
@@ -262,18 +243,16 @@ __device__ __forceinline__ void attend_tile(WaveState<PREC, QG>& w, const unsign
     for (int g = 0; g < QG; ++g) {
       lt[g] = 0.f;
       if constexpr (PREC == kPrecFp8) {
-        // the MFMA starts from -m, so it returns the logit minus the
-        // reference and P needs no per-score arithmetic before exp2; both
-        // chunks' MFMAs are issued before the exponentials of the first, which
-        // then overlap the second's MFMA
-        const f32x16 s0 = chunk_scores<PREC, MASK>(kb, 0, col, hf, w.qf[g], rem, lg, w.neg_m[g]);
-        const f32x16 s1 = chunk_scores<PREC, MASK>(kb, 1, col, hf, w.qf[g], rem, lg, w.neg_m[g]);
-        lt[g] += exp_chunk_shifted(s0, p16[g][0]);
-        lt[g] += exp_chunk_shifted(s1, p16[g][1]);
+        // both chunks' MFMAs are issued before the exponentials of the first,
+        // which then overlap the second's MFMA
+        const f32x16 s0 = chunk_scores<PREC, MASK>(kb, 0, col, hf, w.qf[g], rem);
+        const f32x16 s1 = chunk_scores<PREC, MASK>(kb, 1, col, hf, w.qf[g], rem);
+        lt[g] += exp_chunk(s0, c_scale, -w.m_run[g], p16[g][0]);
+        lt[g] += exp_chunk(s1, c_scale, -w.m_run[g], p16[g][1]);
       } else {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const f32x16 sc = chunk_scores<PREC, MASK>(kb, c, col, hf, w.qf[g], rem, lg);
+          const f32x16 sc = chunk_scores<PREC, MASK>(kb, c, col, hf, w.qf[g], rem);
           lt[g] += exp_chunk(sc, c_scale, -w.m_run[g], p16[g][c]);
         }
       }
@@ -292,21 +271,19 @@ __device__ __forceinline__ void attend_tile(WaveState<PREC, QG>& w, const unsign
         if (__builtin_amdgcn_ballot_w64(over) == 0) continue;
         f32x16 s[2];
 #pragma unroll
-        for (int c = 0; c < 2; ++c) s[c] = chunk_scores<PREC, MASK>(kb, c, col, hf, w.qf[g], rem, lg);
+        for (int c = 0; c < 2; ++c) s[c] = chunk_scores<PREC, MASK>(kb, c, col, hf, w.qf[g], rem);
         const float mt = tile_max(s) * c_scale;
         const float mnew = over ? fmaxf(w.m_run[g], mt) : w.m_run[g];
         const float alpha = __builtin_amdgcn_exp2f(w.m_run[g] - mnew);  // exactly 1 unless over
         w.m_run[g] = mnew;
-        if constexpr (PREC == kPrecFp8) w.neg_m[g] = -mnew;
         w.l_run[g] *= alpha;
         w.o[g][0] *= alpha;
         w.o[g][1] *= alpha;
         f16x8 pn[2][2];
         const float ln = exp_chunk(s[0], c_scale, -mnew, pn[0]) + exp_chunk(s[1], c_scale, -mnew, pn[1]);
         // Rows that did not overflow keep the P (and its sum) of the normal
-        // path: for FP8 that P came from an MFMA started at -m, which can
-        // round differently from exp2(s - m) here, and a row's bits must not
-        // depend on whether a neighbour in its group moved its reference.
+        // path, so that a row's bits never depend on whether a neighbour in
+        // its group moved its reference.
         if (over) {
           lt[g] = ln;
 #pragma unroll
@@ -406,13 +383,12 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
     return;
   }
 
-  // logit (log2 units) = raw dot * lg.c (FP16); FP8: the exponent field of
-  // q_unit = 2^E is the E8M0 operand scale that makes the MFMA return the
-  // logit itself
-  Logit lg = {a.tau_log2e, 127};
+  // logit (log2 units) = raw dot * lg.c; FP8 dots are sums of code
+  // products, so c also carries s_q * s_k
+  Logit lg = {a.tau_log2e};
   float sv = 1.0f;
   if constexpr (PREC == kPrecFp8) {
-    lg = {1.0f, (int)((__float_as_uint(a.q_unit[bh]) >> 23) & 0xFF)};
+    lg = {a.tau_log2e * a.scales[bh] * a.scales[a.bh_count + bh]};
     sv = a.scales[2 * a.bh_count + bh];
   }
 

@@ -29,9 +29,7 @@ struct AttnArgs {
   const void* q;          // head-major [B*H][q_rows_alloc][64]: e4m3 codes or fp16
   const void* kc;         // cache K: [B*H][n_alloc][64] (codes or fp16), rows >= n are 0
   const void* vt;         // cache V: [B*H][n_alloc/64][64 d][64 keys], keys >= n are 0
-  const float* scales;    // device [3][B*H]: s_q, s_k, s_v (the method's scales)
-  const float* q_unit;    // device [B*H]: 2^E, the logit (log2 units) of one unit of the
-                          // FP8 Q operand's code dot product (see launch_fp8_scales)
+  const float* scales;    // device [3][B*H]: s_q, s_k, s_v
   uint16_t* out;          // final mode: fp16 [B][out_rows][H][64]
   uint16_t* part_o;       // split mode: [B*H][q_rows_valid][splits][64] fp16, O / l of the split
   float* part_ml;         // split mode: [B*H][q_rows_valid][splits][2] = (m in log2 units, l)
@@ -63,30 +61,25 @@ struct Factors {
 
 // K0 + scale finalisation: per-(b,h) amax of the scaled context queries, K, V
 // over the first n_b rows of batch element b (n_b: device [B], n_max their
-// maximum), then s = amax/448 (1 if amax = 0) into scales[0 .. 3BH); inv
-// [3BH] gets 448/amax for K and V and, in the Q slot, the inverse scale of
-// the kernels' Q operand, whose logit unit 2^E goes to q_unit [BH] and whose
-// saturation bound goes to q_clamp [BH] (the rule is stated at scales_kernel).
-// amax_bits: device scratch [3*B*H].
+// maximum), then s = amax/448, inv = 448/amax (1 if amax = 0) into
+// scales[0 .. 3BH) and inv[0 .. 3BH).  amax_bits: device scratch [3*B*H].
 hipError_t launch_fp8_scales(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                              const uint16_t* gate, int B, int64_t rows_padded, int64_t n_max,
                              const int64_t* n_b, int H, int mode, const Factors& f,
-                             uint32_t* amax_bits, float* scales, float* inv, float* q_unit,
-                             float* q_clamp, hipStream_t s);
+                             uint32_t* amax_bits, float* scales, float* inv, hipStream_t s);
 
 // Fill `count` floats with a value (FP16 caches get unit scales).
 hipError_t launch_fill_f32(float* p, int64_t count, float value, hipStream_t s);
 
 // K1: scale rows [0, rows_valid) of q [B][rows_in][H][64] (and gate [B][rows_in][H]),
-// optionally quantise with inv_q (device [B*H], NULL = keep fp16; scaled values
-// clamped to +-q_clamp [B*H] first, or +-448 when q_clamp is NULL), and write
+// optionally quantise with inv_q (device [B*H], NULL = keep fp16), and write
 // head-major out [B*H][rows_out][64]; rows in [rows_valid, rows_out) become 0.
 // rows_valid_b (device [B], may be NULL) gives batch element b its own
 // rows_valid.
 hipError_t launch_scale_queries(const uint16_t* q, const uint16_t* gate, int B, int64_t rows_in,
                                 int64_t rows_valid, const int64_t* rows_valid_b, int64_t rows_out,
-                                int H, int mode, const Factors& f, const float* inv_q,
-                                const float* q_clamp, void* out, hipStream_t s);
+                                int H, int mode, const Factors& f, const float* inv_q, void* out,
+                                hipStream_t s);
 
 // K2: K/V rows [0, n_b) of batch element b -> cache (codes with inv_k / inv_v
 // when prec == FP8, else fp16 copies); rows in [n_b, n_alloc) become 0.

@@ -10,9 +10,7 @@
 // kept, so results are bit-identical to the unfused sequence.
 // Quantisation follows "[FP8 3/4] Integrate FP8 attention and caching into
 // TabICLv2" (introduction): per-head scales from the context, with the Q scale
-// taken from the scaled context queries and reused for query rows.  The Q
-// operand of the attention kernels is quantised with a context-derived scale
-// of their own (see scales_kernel).
+// taken from the scaled context queries and reused for query rows.
 //
 // These kernels are HBM-bound: each element is read once, coalesced, 16
 // bytes per lane, and written once.
@@ -30,20 +28,20 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// e4m3 codes of two values, clamped to +-lim (<= 448) first; the hardware
-// conversion rounds to nearest even, first operand in byte 0.
-__device__ inline uint32_t e4m3_pair(float a, float b, float lim = 448.0f) {
-  a = fminf(fmaxf(a, -lim), lim);
-  b = fminf(fmaxf(b, -lim), lim);
+// e4m3 codes of two values (clamped to +-448 first; the hardware conversion
+// rounds to nearest even, first operand in byte 0).
+__device__ inline uint32_t e4m3_pair(float a, float b) {
+  a = fminf(fmaxf(a, -448.0f), 448.0f);
+  b = fminf(fmaxf(b, -448.0f), 448.0f);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
-__device__ inline i32x2 quantize8(const f16x8& x, float inv, float lim = 448.0f) {
+__device__ inline i32x2 quantize8(const f16x8& x, float inv) {
   i32x2 r;
-  r[0] = (int)(e4m3_pair((float)x[0] * inv, (float)x[1] * inv, lim) |
-               (e4m3_pair((float)x[2] * inv, (float)x[3] * inv, lim) << 16));
-  r[1] = (int)(e4m3_pair((float)x[4] * inv, (float)x[5] * inv, lim) |
-               (e4m3_pair((float)x[6] * inv, (float)x[7] * inv, lim) << 16));
+  r[0] = (int)(e4m3_pair((float)x[0] * inv, (float)x[1] * inv) |
+               (e4m3_pair((float)x[2] * inv, (float)x[3] * inv) << 16));
+  r[1] = (int)(e4m3_pair((float)x[4] * inv, (float)x[5] * inv) |
+               (e4m3_pair((float)x[6] * inv, (float)x[7] * inv) << 16));
   return r;
 }
 
@@ -65,7 +63,7 @@ template <int MODE, bool FP8>
 __global__ __launch_bounds__(256) void scale_queries_kernel(
     const f16x8* __restrict__ q, const _Float16* __restrict__ gate, int H, int64_t rows_in,
     int64_t rows_valid_all, const int64_t* __restrict__ rows_valid_b, int64_t rows_out, Factors f,
-    const float* __restrict__ inv_q, const float* __restrict__ q_clamp, void* __restrict__ out) {
+    const float* __restrict__ inv_q, void* __restrict__ out) {
   const int b = blockIdx.y;
   const int64_t rows_valid = rows_valid_b ? rows_valid_b[b] : rows_valid_all;
   const int64_t per_row = (int64_t)H * 8;
@@ -87,9 +85,8 @@ __global__ __launch_bounds__(256) void scale_queries_kernel(
     const int64_t orow = ((int64_t)b * H + h) * rows_out + row;
     if constexpr (FP8) {
       const float inv = inv_q[b * H + h];
-      const float lim = q_clamp ? q_clamp[b * H + h] : 448.0f;
       i32x2 c = {0, 0};
-      if (row < rows_valid) c = quantize8(y, inv, lim);
+      if (row < rows_valid) c = quantize8(y, inv);
       reinterpret_cast<i32x2*>(out)[orow * 8 + d8] = c;
     } else {
       reinterpret_cast<f16x8*>(out)[orow * 8 + d8] = y;
@@ -158,45 +155,14 @@ __global__ void fill_f32_kernel(float* p, int64_t count, float value) {
 
 // Scales from the amaxes [3][B*H] (Q, K, V), the same rule for all three:
 // s = fp32(a / 448), inv = fp32(448 / a), a = 0 giving 1 and 1 (correctly
-// rounded IEEE float32 divisions).  These are the scales of the method; they
-// are what the cache exports.
-//
-// The Q operand the attention kernels multiply is quantised with a scale of
-// their own (a kernel-only choice; its codes are not the method's Q codes):
-// the one for which the logit of one unit of sum_d q_code k_code is a power
-// of two, q_unit = 2^E, so that the FP8 QK MFMA applies the whole logit
-// factor through its E8M0 operand scale.  With base = fp32(log2(e)/sqrt(D)) *
-// s_k and a' = a_q (448 when a_q = 0, the amax that s_q = 1 stands for), E is
-// the smallest integer with fp32(a' * base) <= 448 * 2^E, inv_q = base * 2^-E
-// and q_unit = 2^E.  Scaled queries are clamped to +-q_clamp = fp32(a' *
-// inv_q) before rounding, the image of the context amax, so that query rows
-// above it saturate where the method's codes do (at +-448 of s_q, i.e. at
-// the amax), not up to twice as far out.  It all depends on (s_q, s_k) only,
-// so an imported cache derives the same values from the exported scales.
+// rounded IEEE float32 divisions).
 __global__ void scales_kernel(const uint32_t* __restrict__ amax_bits, int count,
-                              float* __restrict__ scales, float* __restrict__ inv,
-                              float* __restrict__ q_unit, float* __restrict__ q_clamp) {
+                              float* __restrict__ scales, float* __restrict__ inv) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= count) return;
-  const int bh_count = count / 3;
   const float a = __uint_as_float(amax_bits[i]);
   scales[i] = a == 0.f ? 1.f : a / 448.0f;
-  if (i >= bh_count) {
-    inv[i] = a == 0.f ? 1.f : 448.0f / a;
-    return;
-  }
-  const float ak = __uint_as_float(amax_bits[bh_count + i]);
-  const float s_k = ak == 0.f ? 1.f : ak / 448.0f;
-  const float base = kLog2eTau * s_k;
-  const float a1 = a == 0.f ? 448.0f : a;
-  const float v = a1 * base;
-  int e = (int)ceilf(log2f(v / 448.0f));
-  while (ldexpf(448.0f, e) < v) ++e;
-  while (ldexpf(448.0f, e - 1) >= v) --e;
-  const float iq = ldexpf(base, -e);
-  q_unit[i] = ldexpf(1.0f, e);
-  inv[i] = iq;
-  q_clamp[i] = a1 * iq;
+  inv[i] = a == 0.f ? 1.f : 448.0f / a;
 }
 
 // ---------------------------------------------------------------- K2
@@ -277,8 +243,7 @@ hipError_t launch_fill_f32(float* p, int64_t count, float value, hipStream_t s) 
 hipError_t launch_fp8_scales(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                              const uint16_t* gate, int B, int64_t rows_padded, int64_t n_max,
                              const int64_t* n_b, int H, int mode, const Factors& f,
-                             uint32_t* amax_bits, float* scales, float* inv, float* q_unit,
-                             float* q_clamp, hipStream_t s) {
+                             uint32_t* amax_bits, float* scales, float* inv, hipStream_t s) {
   const int count = 3 * B * H;
   hipLaunchKernelGGL(fill_u32_kernel, dim3(1), dim3(256), 0, s, amax_bits, (int64_t)count, 0u);
   const int per_row = H * 8;
@@ -297,22 +262,21 @@ hipError_t launch_fp8_scales(const uint16_t* q, const uint16_t* k, const uint16_
     hipLaunchKernelGGL(amax_kernel<kScaleLog>, grid, dim3(block), lds, s, qv, kv, vv, gv, H, rows_padded, n_b, rows_per_block, f, amax_bits);
   else
     hipLaunchKernelGGL(amax_kernel<kScaleGated>, grid, dim3(block), lds, s, qv, kv, vv, gv, H, rows_padded, n_b, rows_per_block, f, amax_bits);
-  hipLaunchKernelGGL(scales_kernel, dim3((count + 255) / 256), dim3(256), 0, s, amax_bits, count, scales, inv,
-                     q_unit, q_clamp);
+  hipLaunchKernelGGL(scales_kernel, dim3((count + 255) / 256), dim3(256), 0, s, amax_bits, count, scales, inv);
   return hipGetLastError();
 }
 
 hipError_t launch_scale_queries(const uint16_t* q, const uint16_t* gate, int B, int64_t rows_in,
                                 int64_t rows_valid, const int64_t* rows_valid_b, int64_t rows_out,
-                                int H, int mode, const Factors& f, const float* inv_q,
-                                const float* q_clamp, void* out, hipStream_t s) {
+                                int H, int mode, const Factors& f, const float* inv_q, void* out,
+                                hipStream_t s) {
   const int64_t items = rows_out * H * 8;
   const dim3 grid((unsigned)grid_for(items, 256, 4096), (unsigned)B);
   auto qv = reinterpret_cast<const f16x8*>(q);
   auto gv = reinterpret_cast<const _Float16*>(gate);
 #define SDM_K1(MODE, FP8)                                                                     \
   hipLaunchKernelGGL((scale_queries_kernel<MODE, FP8>), grid, dim3(256), 0, s, qv, gv, H,      \
-                     rows_in, rows_valid, rows_valid_b, rows_out, f, inv_q, q_clamp, out)
+                     rows_in, rows_valid, rows_valid_b, rows_out, f, inv_q, out)
   const bool fp8 = inv_q != nullptr;
   if (mode == kScaleNone) { if (fp8) SDM_K1(kScaleNone, true); else SDM_K1(kScaleNone, false); }
   else if (mode == kScaleLog) { if (fp8) SDM_K1(kScaleLog, true); else SDM_K1(kScaleLog, false); }

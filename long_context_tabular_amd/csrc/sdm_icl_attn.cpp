@@ -34,13 +34,11 @@ struct sdm_icl_cache_s {
   std::vector<float> L32;         // L32 of each batch element
   std::vector<uint16_t> kh;       // fp16 bits of k_h per (b, h) ([B*H], empty for NONE)
   void* block;     // one device allocation: [kc][vt][meta], meta = [scales 3BH][inv 3BH]
-                   // [q_unit BH][q_clamp BH][n_b B][k_h BH]
+                   // [n_b B][k_h BH]
   void* kc;
   void* vt;
   float* scales;
   float* inv;
-  float* q_unit;
-  float* q_clamp;
   int64_t* n_dev;
   uint16_t* kh_dev;
   size_t bytes;
@@ -272,7 +270,6 @@ AttnArgs attn_args(const sdm_icl_cache_s* c) {
   a.kc = c->kc;
   a.vt = c->vt;
   a.scales = c->scales;
-  a.q_unit = c->q_unit;
   a.n_b = c->n_dev;
   a.n_alloc = c->n_alloc;
   a.heads = c->H;
@@ -281,27 +278,24 @@ AttnArgs attn_args(const sdm_icl_cache_s* c) {
   return a;
 }
 
-// Point scales / inv / q_unit / q_clamp / n_b / k_h into a metadata region
-// laid out as [scales 3BH][inv 3BH][q_unit BH][q_clamp BH][n_b B][k_h BH]
-// (for an offloaded cache that region is the whole device block).
+// Point scales / inv / n_b / k_h into a metadata region laid out as
+// [scales 3BH][inv 3BH][n_b B][k_h BH] (for an offloaded cache that region is
+// the whole device block).
 void set_meta(sdm_icl_cache_s* c, void* meta) {
   const int64_t BH = (int64_t)c->B * c->H;
   c->scales = (float*)meta;
   c->inv = c->scales + 3 * BH;
-  c->q_unit = c->scales + 6 * BH;
-  c->q_clamp = c->scales + 7 * BH;
-  c->n_dev = (int64_t*)((char*)meta + 8 * BH * sizeof(float));
+  c->n_dev = (int64_t*)((char*)meta + 6 * BH * sizeof(float));  // 24 BH bytes: 8-byte aligned
   c->kh_dev = (uint16_t*)((char*)c->n_dev + c->B * sizeof(int64_t));
 }
 
-// Bytes of the float section of a cache's metadata: scales, inverse scales,
-// q_unit and q_clamp per (b, h) (8 floats, so n_b after it is 8-byte aligned).
-size_t scale_bytes(int64_t BH) { return (size_t)8 * BH * sizeof(float); }
+// Bytes of the float section of a cache's metadata: scales and inverse scales
+// of Q, K and V per (b, h).
+size_t scale_bytes(int64_t BH) { return (size_t)6 * BH * sizeof(float); }
 
 // A cache object with its lengths, length scalars, head factors and split
 // plan, and its one device allocation ([kc][vt][meta]) with n_b and k_h
-// uploaded; K/V, scales, inverse scales and q_unit are left for the caller
-// to fill.
+// uploaded; K/V, scales and inverse scales are left for the caller to fill.
 sdm_icl_status new_cache(int B, int H, const int64_t* lengths, int mode, int prec, const float* coef,
                          int dev, int cus, hipStream_t s, const char* who, sdm_icl_cache_s** out) {
   int64_t n = 0;
@@ -408,44 +402,22 @@ float f16_bits_to_f32(uint16_t h) {
   return v;
 }
 
-uint32_t float_bits(float x) {
-  uint32_t b;
-  std::memcpy(&b, &x, sizeof b);
-  return b;
-}
 
-// The fp16 amax a behind a scale s = fp32(a / 448) that fit derived: a is the
-// one fp16 value whose quotient by 448 rounds to s (distinct fp16 values
-// differ by at least 2^-11 relative, so their fp32 quotients differ).  s = 1
-// stands for a = 0 or a = 448, which give the same scale and inverse scale;
-// it is reported as 448.
-bool amax_from_scale(float s, float* amax) {
+// The inverse scale fit derived together with s = fp32(a / 448), where a is
+// the fp16 amax: a is the one fp16 value whose quotient by 448 rounds to s
+// (distinct fp16 values differ by at least 2^-11 relative, so their fp32
+// quotients differ).  s = 1 stands for a = 0 or a = 448, both giving inv = 1.
+bool inverse_from_scale(float s, float* inv) {
   if (!(s > 0.f) || !std::isfinite(s)) return false;
-  if (s == 1.f) { *amax = 448.f; return true; }
+  if (s == 1.f) { *inv = 1.f; return true; }
   const uint16_t h0 = f32_to_f16_bits(s * 448.0f);
   for (int d = -1; d <= 1; ++d) {
     const uint16_t h = (uint16_t)(h0 + d);
     const float a = f16_bits_to_f32(h);
     if (!(a > 0.f) || !std::isfinite(a)) continue;
-    if (a / 448.0f == s) { *amax = a; return true; }
+    if (a / 448.0f == s) { *inv = 448.0f / a; return true; }
   }
   return false;
-}
-
-// The attention kernels' own Q operand scale (the host twin of the rule in
-// prep.hip's scales_kernel): base = fp32(log2(e)/sqrt(D)) * s_k, E the
-// smallest integer with fp32(a_q * base) <= 448 * 2^E, inv_q = base * 2^-E,
-// q_unit = 2^E, q_clamp = fp32(a_q * inv_q); a_q = 448 stands in for an
-// all-zero Q (s_q = 1).
-void q_operand_scale(float a_q, float s_k, float* inv_q, float* q_unit, float* q_clamp) {
-  const float base = kLog2eTau * s_k;
-  const float v = a_q * base;
-  int e = (int)std::ceil(std::log2((double)v / 448.0));
-  while (std::ldexp(448.0f, e) < v) ++e;
-  while (std::ldexp(448.0f, e - 1) >= v) --e;
-  *q_unit = std::ldexp(1.0f, e);
-  *inv_q = std::ldexp(base, -e);
-  *q_clamp = a_q * *inv_q;
 }
 
 
@@ -642,9 +614,9 @@ sdm_icl_status sdm_icl_attn_fit(const sdm_icl_fit_args* a, sdm_icl_cache* out) {
   if (prec == SDM_ICL_PREC_FP8_E4M3) {
     TimedLaunch tl(SDM_ICL_TIMING_PREP, s);
     e = launch_fp8_scales(q16, k16, v16, g16, B, a->rows_padded, n, c->n_dev, H, a->scale_mode, fac,
-                          amax, c->scales, c->inv, c->q_unit, c->q_clamp, s);
+                          amax, c->scales, c->inv, s);
   } else {
-    e = launch_fill_f32(c->scales, 8 * (int64_t)B * H, 1.0f, s);
+    e = launch_fill_f32(c->scales, 6 * (int64_t)B * H, 1.0f, s);
   }
   if (e == hipSuccess) {
     TimedLaunch tl(SDM_ICL_TIMING_PREP, s);
@@ -655,7 +627,7 @@ sdm_icl_status sdm_icl_attn_fit(const sdm_icl_fit_args* a, sdm_icl_cache* out) {
     {
       TimedLaunch tl(SDM_ICL_TIMING_SCALE, s);
       e = launch_scale_queries(q16, g16, B, a->rows_padded, n, c->n_dev, q_rows_alloc, H, a->scale_mode,
-                               fac, prec == SDM_ICL_PREC_FP8_E4M3 ? c->inv : nullptr, c->q_clamp, qctx, s);
+                               fac, prec == SDM_ICL_PREC_FP8_E4M3 ? c->inv : nullptr, qctx, s);
     }
     if (e == hipSuccess) {
       AttnArgs at = attn_args(c);
@@ -731,7 +703,7 @@ sdm_icl_status sdm_icl_attn_query(sdm_icl_cache c, const void* q, const void* ga
     const Factors fac{c->kh_dev, HeadFactors{}};
     e = launch_scale_queries((const uint16_t*)q, (const uint16_t*)gate, c->B, R, R, nullptr,
                              L.q_rows_alloc, c->H, c->mode, fac,
-                             c->prec == SDM_ICL_PREC_FP8_E4M3 ? c->inv : nullptr, c->q_clamp, qbuf, s);
+                             c->prec == SDM_ICL_PREC_FP8_E4M3 ? c->inv : nullptr, qbuf, s);
   }
   if (e != hipSuccess) return hip_fail(e, "query: scale launch");
   AttnArgs at = attn_args(c);
@@ -868,23 +840,18 @@ sdm_icl_status sdm_icl_attn_cache_import(const sdm_icl_import_args* a, sdm_icl_c
   }
   const bool fp8 = a->precision == SDM_ICL_PREC_FP8_E4M3;
   const int64_t eb = fp8 ? 1 : 2, BH = (int64_t)B * H;
-  // the scales, the inverse scales and q_unit they imply (the metadata's
-  // float section): K and V first, then the Q slot, whose operand scale
-  // follows from its amax and s_k
-  std::vector<float> sc(8 * BH, 1.0f);
-  for (int64_t i = 3 * BH - 1; i >= 0; --i) {
+  // the scales and the inverse scales they imply (the metadata's float section)
+  std::vector<float> sc(6 * BH, 1.0f);
+  for (int64_t i = 0; i < 3 * BH; ++i) {
     const float sv = a->host_scales[i];
     if (!fp8) {
       if (sv != 1.f) return fail(SDM_ICL_E_INVALID, "import: FP16 caches have unit scales");
       continue;
     }
-    float amax;
-    if (!amax_from_scale(sv, &amax))
+    if (!inverse_from_scale(sv, &sc[3 * BH + i]))
       return fail(SDM_ICL_E_INVALID, "import: scale %lld (%g) is not fp32(amax/448) of an fp16 amax",
                   (long long)i, (double)sv);
     sc[i] = sv;
-    if (i >= BH) sc[3 * BH + i] = sv == 1.f ? 1.f : 448.0f / amax;
-    else q_operand_scale(amax, sc[BH + i], &sc[3 * BH + i], &sc[6 * BH + i], &sc[7 * BH + i]);
   }
   // host images of the device layout: K [bh][n_alloc][64], V [bh][tiles][64 d][64 keys]
   const int64_t n_alloc = round_up(n, kKeyTile), tiles = n_alloc / kKeyTile;
@@ -1087,8 +1054,7 @@ sdm_icl_status sdm_icl_log_scale(const void* q, const void* gate, int32_t batch,
   TimedLaunch tl(SDM_ICL_TIMING_SCALE, (hipStream_t)stream);
   const Factors fac{nullptr, kh};
   hipError_t e = launch_scale_queries((const uint16_t*)q, (const uint16_t*)gate, batch, rows, rows, nullptr,
-                                      rows, heads, scale_mode, fac, q_inv_scale, nullptr, out,
-                                      (hipStream_t)stream);
+                                      rows, heads, scale_mode, fac, q_inv_scale, out, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "log_scale: launch");
   return SDM_ICL_OK;
 }

@@ -289,7 +289,7 @@ def test_import_validates_before_touching_the_device():
 def test_import_accepts_the_scale_of_every_fp16_amax():
     """fit writes s = fp32(a/448) for an fp16 amax a, for Q, K and V alike;
     import must recognise every such s (it recovers a, and with it the exact
-    inverse scale and the kernels' Q operand scale)."""
+    inverse scale)."""
     k = np.zeros((1, 1, 1, 64), dtype=np.uint8)
     a = _all_finite_fp16_positive()
     bad = []
