@@ -132,6 +132,28 @@ def test_gate_factor_over_every_fp16_gate():
                   <= np.spacing(np.abs(t).astype(np.float16)).astype(np.float64) / 2 + 1e-12)
 
 
+def test_gated_scaling_equals_eager_fp16_passes():
+    """The page describes the unfused path as separate eager passes in fp16
+    ("Fuse shared-length query scaling during inference", Problem
+    identified): PyTorch's own fp16 CPU ops, tanh, then 1 + t, then the two
+    products, must give the oracle's scaled queries bit for bit, over every
+    finite fp16 gate value."""
+    g = _all_finite_fp16()
+    u_eager = (1 + torch.tanh(torch.from_numpy(g.copy()))).numpy()
+    np.testing.assert_array_equal(icl.gate_factor(g).view(np.uint16), u_eager.view(np.uint16))
+    rng = np.random.default_rng(8)
+    H = 4
+    gates = g[: (g.size // H) * H].reshape(-1, H)
+    q = (rng.standard_normal((gates.shape[0], H, 64)) / 8).astype(np.float16)
+    kh = icl.head_factors(icl.length_scalar(40000), np.array([0.5, 0.9, 1.2, 1.5], np.float32))
+    tq, tk, tg = torch.from_numpy(q), torch.from_numpy(kh.copy()), torch.from_numpy(gates.copy())
+    eager = ((tq * tk[:, None]) * (1 + torch.tanh(tg))[..., None]).numpy()
+    np.testing.assert_array_equal(icl.scale_queries(q, icl.SCALE_GATED_LOG, kh, gates).view(np.uint16),
+                                  eager.view(np.uint16))
+    np.testing.assert_array_equal(icl.scale_queries(q, icl.SCALE_LOG, kh).view(np.uint16),
+                                  (tq * tk[:, None]).numpy().view(np.uint16))
+
+
 # --------------------------------------------------------------------------- fp8 scales
 
 def test_fp8_scale_maps_amax_to_448_and_bounds_error():
