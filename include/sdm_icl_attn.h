@@ -166,6 +166,27 @@ sdm_icl_status sdm_icl_attn_query(sdm_icl_cache cache, const void* q, const void
                                   int64_t n_query, void* out, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/* sdm_icl_attn_query for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and results, bit for bit, with the workspace
+ * taken from a scratch array the library holds on each GPU (64 MiB per
+ * device, SDM_ICL_NOALLOC_SCRATCH_BYTES, kept from the library's load until
+ * the process ends).  The call allocates nothing: no hipMalloc, no
+ * hipFree, no allocating library routine, no events (kernel timing is
+ * skipped).  A query whose workspace (query_workspace_size) exceeds the
+ * scratch array, e.g. 1,024 rows at 8 heads and 128 KV splits, returns
+ * SDM_ICL_E_INVALID with the sizes in the message; an offloaded cache
+ * returns SDM_ICL_E_UNSUPPORTED (its streamed chunks need staging space).
+ * Every call on one GPU shares that GPU's array, so calls that overlap on
+ * one GPU (on different streams, or from different threads without
+ * ordering) race and may return wrong rows; calls ordered on one stream are
+ * safe.  Nothing in the array needs clearing between calls: every byte a
+ * call reads it wrote earlier in the same call.  Arguments and errors
+ * otherwise as sdm_icl_attn_query. */
+#define SDM_ICL_NOALLOC_SCRATCH_BYTES (64u << 20)
+sdm_icl_status sdm_icl_attn_query_noalloc(sdm_icl_cache cache, const void* q, const void* gate,
+                                          int64_t n_query, void* out, void* stream);
+
 /* Shape, precision and split plan of a cache. */
 sdm_icl_status sdm_icl_attn_cache_info(sdm_icl_cache cache, sdm_icl_cache_info* info);
 
@@ -338,7 +359,7 @@ int32_t sdm_icl_scope_fp8(void);
  * the pages raise for a misused FP8 cache ("[FP8 3/4] ...", walkthrough). */
 const char* sdm_icl_last_error(void);
 
-/* ABI version (major * 100 + minor). */
+/* ABI version (major * 100 + minor): 102. */
 int32_t sdm_icl_version(void);
 
 #ifdef __cplusplus

@@ -70,6 +70,8 @@ _SIGNATURES = {
     "sdm_icl_attn_query": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_size_t, ctypes.c_void_p]),
+    "sdm_icl_attn_query_noalloc": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                    ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
     "sdm_icl_attn_cache_info": (ctypes.c_int32, [ctypes.c_void_p, ctypes.POINTER(CacheInfo)]),
     "sdm_icl_attn_cache_export": (ctypes.c_int32, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                                    ctypes.c_void_p, ctypes.c_void_p]),
@@ -244,6 +246,7 @@ def sdm_icl_split_plan(n: int, num_cus: int, bh_count: int):
     return s.value, k.value
 
 
+SDM_ICL_NOALLOC_SCRATCH_BYTES = 64 << 20
 SDM_ICL_TIMING_CONTEXT, SDM_ICL_TIMING_QUERY, SDM_ICL_TIMING_COMBINE = 0, 1, 2
 SDM_ICL_TIMING_SCALE, SDM_ICL_TIMING_PREP, SDM_ICL_TIMING_PROJECT = 3, 4, 5
 
@@ -348,6 +351,24 @@ def sdm_icl_attn_query(cache: Cache, q, gate=None, out=None, workspace=None, str
                                         _dev_ptr(gate, "gate", torch.float16), R,
                                         _dev_ptr(out, "out", torch.float16),
                                         _dev_ptr(workspace, "workspace"), ws_bytes, _stream_ptr(stream)))
+    return out
+
+
+def sdm_icl_attn_query_noalloc(cache: Cache, q, gate=None, out=None, stream=None):
+    """sdm_icl_attn_query on the library's per-device scratch array (no
+    workspace argument, no device allocation inside the call); returns ``out``."""
+    import torch
+    B, R, H, D = q.shape
+    if gate is not None and tuple(gate.shape) != (B, R, H):
+        raise ValueError("gate must be [B, R, H]")
+    if out is None:
+        out = torch.empty_like(q)
+    elif tuple(out.shape) != (B, R, H, D):
+        raise ValueError("out must have the shape of q")
+    with _c_scope():
+        _check(lib().sdm_icl_attn_query_noalloc(cache.handle, _dev_ptr(q, "q", torch.float16),
+                                                _dev_ptr(gate, "gate", torch.float16), R,
+                                                _dev_ptr(out, "out", torch.float16), _stream_ptr(stream)))
     return out
 
 

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_NAME = "libsdm_icl_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["prep.hip", "attention.hip", "projection.hip", "sdm_icl_attn.cpp"]
+SOURCES = ["prep.hip", "attention.hip", "projection.hip", "noalloc.hip", "sdm_icl_attn.cpp"]
 # per-source flags: the attention kernels use LLVM's iterative
 # maximum-occupancy machine scheduler (measured 2.6% faster on the 512K
 # context pass than the max-ILP strategy, itself ~5% faster than the default)

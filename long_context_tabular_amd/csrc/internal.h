@@ -19,6 +19,13 @@ constexpr float kLog2eTau = (float)(1.4426950408889634 / 8.0);
 constexpr int kScaleNone = 0, kScaleLog = 1, kScaleGated = 2;
 constexpr int kPrecFp16 = 0, kPrecFp8 = 1;
 
+// Bytes of the per-device scratch array behind sdm_icl_attn_query_noalloc.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+
+// Device address of that scratch array on `device`, which must be the current
+// device; looked up once per device (hipGetSymbolAddress) and kept.
+hipError_t noalloc_scratch(int device, void** ptr);
+
 // Per-head fp16 factors k_h (bit patterns), passed by value to the kernels.
 struct HeadFactors {
   uint16_t bits[kMaxHeads];

@@ -206,8 +206,9 @@ struct TimedLaunch {
   bool on = false;
   TimingRec rec{};
   hipStream_t s;
-  TimedLaunch(int cls, hipStream_t stream) : s(stream) {
-    {
+  // enable = false: never time (no event is created), whatever the setting
+  TimedLaunch(int cls, hipStream_t stream, bool enable = true) : s(stream) {
+    if (enable) {
       std::lock_guard<std::mutex> lk(g_timing_mu);
       on = g_timing_on;
     }
@@ -491,7 +492,7 @@ hipError_t streamed_attention(sdm_icl_cache_s* c, AttnArgs at, char* w, const Qu
 
 extern "C" {
 
-int32_t sdm_icl_version(void) { return 101; }
+int32_t sdm_icl_version(void) { return 102; }
 
 const char* sdm_icl_last_error(void) { return g_error.c_str(); }
 
@@ -665,47 +666,65 @@ sdm_icl_status sdm_icl_attn_query_workspace_size(sdm_icl_cache c, int64_t n_quer
   return SDM_ICL_OK;
 }
 
-sdm_icl_status sdm_icl_attn_query(sdm_icl_cache c, const void* q, const void* gate, int64_t R,
-                                  void* out, void* ws, size_t ws_bytes, void* stream) {
-  if (!live(c)) return fail(SDM_ICL_E_STATE, "query: unknown or released cache");
+}  // extern "C"
+
+namespace {
+
+// One query call on a workspace of ws_bytes at ws (the caller's, or the
+// scratch array of the no-allocation entry point); `who` names the entry
+// point in error messages.
+sdm_icl_status query_impl(sdm_icl_cache c, const void* q, const void* gate, int64_t R, void* out,
+                          void* ws, size_t ws_bytes, void* stream, bool scratch) {
+  const char* who = scratch ? "query_noalloc" : "query";
+  if (!live(c)) return fail(SDM_ICL_E_STATE, "%s: unknown or released cache", who);
   if (c->scoped && !scope_fp8())
-    return fail(SDM_ICL_E_STATE, "query: an FP8 cache built under the FP8 scope is used outside an enabled scope");
-  if (R < 0) return fail(SDM_ICL_E_INVALID, "query: n_query < 0");
+    return fail(SDM_ICL_E_STATE, "%s: an FP8 cache built under the FP8 scope is used outside an enabled scope", who);
+  if (R < 0) return fail(SDM_ICL_E_INVALID, "%s: n_query < 0", who);
   if ((gate != nullptr) != (c->mode == SDM_ICL_SCALE_GATED_LOG))
     return fail(SDM_ICL_E_INVALID, c->mode == SDM_ICL_SCALE_GATED_LOG
-                                       ? "query: the cache was fitted with GATED_LOG; a gate is required"
-                                       : "query: the cache was not fitted with GATED_LOG; gate must be NULL");
+                                       ? "%s: the cache was fitted with GATED_LOG; a gate is required"
+                                       : "%s: the cache was not fitted with GATED_LOG; gate must be NULL", who);
   if (R == 0) return SDM_ICL_OK;
-  if (!q || !out || !ws) return fail(SDM_ICL_E_INVALID, "query: q, out and workspace are required");
+  if (scratch && c->offloaded)
+    return fail(SDM_ICL_E_UNSUPPORTED, "%s: the cache is offloaded to host memory; its streamed queries need "
+                                       "staging buffers: use sdm_icl_attn_query with a workspace", who);
+  if (!q || !out || (!ws && !scratch)) return fail(SDM_ICL_E_INVALID, "%s: q, out and workspace are required", who);
   if (!aligned(q, 16) || !aligned(out, 16) || !aligned(ws, 16))
-    return fail(SDM_ICL_E_INVALID, "query: q, out and workspace must be 16-byte aligned");
-  if (!aligned(gate, 2)) return fail(SDM_ICL_E_INVALID, "query: gate must be 2-byte aligned");
-  if ((int64_t)c->B * R * c->H > (int64_t)1 << 40) return fail(SDM_ICL_E_INVALID, "query: too many rows");
+    return fail(SDM_ICL_E_INVALID, "%s: q, out and workspace must be 16-byte aligned", who);
+  if (!aligned(gate, 2)) return fail(SDM_ICL_E_INVALID, "%s: gate must be 2-byte aligned", who);
+  if ((int64_t)c->B * R * c->H > (int64_t)1 << 40) return fail(SDM_ICL_E_INVALID, "%s: too many rows", who);
   const QueryLayout L = query_layout(c, R);
-  if (ws_bytes < L.total)
-    return fail(SDM_ICL_E_STATE, "query: workspace of %zu bytes is smaller than the %zu needed", ws_bytes, L.total);
+  if (scratch && L.total > kNoAllocScratchBytes)
+    return fail(SDM_ICL_E_INVALID, "%s: %lld query rows need %zu bytes of scratch, more than the %zu the library "
+                                   "holds per device; use sdm_icl_attn_query with a workspace",
+                who, (long long)R, L.total, kNoAllocScratchBytes);
+  if (!scratch && ws_bytes < L.total)
+    return fail(SDM_ICL_E_STATE, "%s: workspace of %zu bytes is smaller than the %zu needed", who, ws_bytes, L.total);
   int dev;
   DeviceInfo di;
   sdm_icl_status st = current_device(&dev, &di);
   if (st) return st;
-  if (dev != c->device) return fail(SDM_ICL_E_DEVICE, "query: cache lives on device %d, current is %d", c->device, dev);
-  const void* ptrs[] = {q, gate, out, ws};
+  if (dev != c->device) return fail(SDM_ICL_E_DEVICE, "%s: cache lives on device %d, current is %d", who, c->device, dev);
+  const void* ptrs[] = {q, gate, out, scratch ? nullptr : ws};
   const char* names[] = {"q", "gate", "out", "workspace"};
   for (int i = 0; i < 4; ++i)
     if (ptrs[i] && (st = check_device_ptr(ptrs[i], dev, names[i]))) return st;
-
+  if (scratch) {
+    hipError_t e = noalloc_scratch(dev, &ws);
+    if (e != hipSuccess) return hip_fail(e, "query_noalloc: scratch address");
+  }
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
   void* qbuf = w + L.q_off;
   hipError_t e;
   {
-    TimedLaunch tl(SDM_ICL_TIMING_SCALE, s);
+    TimedLaunch tl(SDM_ICL_TIMING_SCALE, s, !scratch);
     const Factors fac{c->kh_dev, HeadFactors{}};
     e = launch_scale_queries((const uint16_t*)q, (const uint16_t*)gate, c->B, R, R, nullptr,
                              L.q_rows_alloc, c->H, c->mode, fac,
                              c->prec == SDM_ICL_PREC_FP8_E4M3 ? c->inv : nullptr, qbuf, s);
   }
-  if (e != hipSuccess) return hip_fail(e, "query: scale launch");
+  if (e != hipSuccess) return hip_fail(e, scratch ? "query_noalloc: scale launch" : "query: scale launch");
   AttnArgs at = attn_args(c);
   at.q = qbuf;
   at.q_rows_alloc = L.q_rows_alloc;
@@ -722,21 +741,35 @@ sdm_icl_status sdm_icl_attn_query(sdm_icl_cache c, const void* q, const void* ga
     at.part_o = (uint16_t*)(w + L.po_off);
     at.part_ml = (float*)(w + L.ml_off);
     {
-      TimedLaunch tl(SDM_ICL_TIMING_QUERY, s);
+      TimedLaunch tl(SDM_ICL_TIMING_QUERY, s, !scratch);
       e = launch_attention(at, c->prec, true, s);
     }
     if (e == hipSuccess) {
-      TimedLaunch tl(SDM_ICL_TIMING_COMBINE, s);
+      TimedLaunch tl(SDM_ICL_TIMING_COMBINE, s, !scratch);
       e = launch_combine(at.part_o, at.part_ml, c->scales + 2 * c->B * c->H, c->B, c->H, R, c->splits,
                          c->prec, (uint16_t*)out, s);
     }
   } else {
     at.out = (uint16_t*)out;
-    TimedLaunch tl(SDM_ICL_TIMING_QUERY, s);
+    TimedLaunch tl(SDM_ICL_TIMING_QUERY, s, !scratch);
     e = launch_attention(at, c->prec, false, s);
   }
-  if (e != hipSuccess) return hip_fail(e, "query: attention launch");
+  if (e != hipSuccess) return hip_fail(e, scratch ? "query_noalloc: attention launch" : "query: attention launch");
   return SDM_ICL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sdm_icl_status sdm_icl_attn_query(sdm_icl_cache c, const void* q, const void* gate, int64_t R,
+                                  void* out, void* ws, size_t ws_bytes, void* stream) {
+  return query_impl(c, q, gate, R, out, ws, ws_bytes, stream, false);
+}
+
+sdm_icl_status sdm_icl_attn_query_noalloc(sdm_icl_cache c, const void* q, const void* gate, int64_t R,
+                                          void* out, void* stream) {
+  return query_impl(c, q, gate, R, out, nullptr, 0, stream, true);
 }
 
 sdm_icl_status sdm_icl_attn_cache_info(sdm_icl_cache c, sdm_icl_cache_info* info) {

@@ -34,7 +34,16 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), f"missing export {n}"
     assert set(names) == set(B._SIGNATURES), "binding and header disagree"
-    assert B.sdm_icl_version() == 101
+    assert B.sdm_icl_version() == 102
+
+
+def test_noalloc_query_validates_on_the_host():
+    """The no-allocation query rejects an unknown handle before any device
+    call (no GPU needed), like the workspace query."""
+    lib = B.lib()
+    assert lib.sdm_icl_attn_query_noalloc(None, None, None, 4, None, None) == 6
+    assert "unknown or released cache" in B.sdm_icl_last_error()
+    assert "query_noalloc" in B.sdm_icl_last_error()
 
 
 @pytest.mark.parametrize("n", [0, 1, 2, 3, 1000, 1024, 8192, 16384, 65537, 131072, 523288, 524288, 10**9])
