@@ -20,7 +20,9 @@
 //   * Q stays in VGPRs for the whole KV loop (MFMA B operand).
 //   * 64-key tiles of K and of V are fetched as separate loads into registers
 //     two tiles ahead, and written into separate double-buffered LDS stages
-//     (K row-major, V transposed and widened to fp16), one barrier per tile.
+//     (K row-major, V transposed and widened to fp16): one barrier per tile
+//     for the FP8 context pass, and for the other kernels a barrier after K's
+//     stores and another after V's, so QK^T never waits for V to land.
 //   * S^T = K Q^T with v_mfma_scale_f32_32x32x64_f8f6f4 (FP8) or
 //     32x32x16_f16.  K rows are fed in a permuted order so that each lane
 //     ends up holding, for its own query, exactly the 8-key groups that the
@@ -127,6 +129,15 @@ struct Ops<kPrecFp16> {
 
 constexpr int kVRow = 144;  // LDS bytes per d-row of the fp16 V^T tile (128 + 16 pad)
 
+// Stage each tile's K and V behind separate barriers (see advance()): the
+// tile's QK^T and softmax start once K is in LDS, and V's stores (and FP8
+// widening) go on in their shadow.  Measured against one barrier per tile on
+// one box: the FP16 16K context pass 1.8% and the 128-row cached query kernel
+// 2% faster, the FP8 context passes 1.2% (512K) to 2.8% (128K) slower, so the
+// FP8 context kernel keeps the single barrier.
+template <int PREC, bool SPLIT>
+constexpr bool split_barrier() { return PREC == kPrecFp16 || SPLIT; }
+
 // Staging registers of one thread for one K tile and one V tile: R chunks of
 // 16 d of one key (K, row-major) and 16 keys of one d (V, tile-transposed).
 template <int EB, int R>
@@ -213,10 +224,12 @@ __device__ __forceinline__ f32x16 chunk_scores(const unsigned char* kb, int c, i
 // (one chunk of scores live); FP8 issues both chunks' MFMAs of a group first
 // (two live), so that the first chunk's exponentials overlap the second's
 // MFMA.  The rare overflow path recomputes the scores instead of keeping them.
-template <int PREC, int QG, bool FIRST, bool MASK>
+// `mid` runs between the softmax and the PV product (a barrier that makes the
+// tile's V stage visible, when V is staged after K).
+template <int PREC, int QG, bool FIRST, bool MASK, class Mid>
 __device__ __forceinline__ void attend_tile(WaveState<PREC, QG>& w, const unsigned char* kb,
                                             const unsigned char* vb, Logit lg, int col,
-                                            int hf, int rem) {
+                                            int hf, int rem, Mid&& mid) {
   const float c_scale = lg.c;
   f16x8 p16[QG][2][2];
   // FP8: ask the scheduler to interleave the MFMAs with the tile's other
@@ -297,6 +310,8 @@ __device__ __forceinline__ void attend_tile(WaveState<PREC, QG>& w, const unsign
     for (int g = 0; g < QG; ++g) w.l_run[g] += lt[g];
   }
 
+  mid();
+
   // ---- O^T += V^T P^T
   if constexpr (PREC == kPrecFp8) __builtin_amdgcn_iglp_opt(0);
 #pragma unroll
@@ -323,7 +338,7 @@ __device__ __forceinline__ void set_wave_priority(int p) {
   }
 }
 
-template <int PREC, int QG, bool SPLIT, int W>
+template <int PREC, int QG, bool SPLIT, int W, bool SB = split_barrier<PREC, SPLIT>()>
 __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
   typedef Ops<PREC> O;
   constexpr int EB = O::EB;
@@ -455,12 +470,18 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
       for (int c = 0; c < EB; ++c) st.v[i][c] = vp[c];
     }
   };
-  auto store_stage = [&](int buf, const Stage<EB, R>& st) {
+  auto store_k = [&](int buf, const Stage<EB, R>& st) {
 #pragma unroll
     for (int i = 0; i < R; ++i) {
-      const int kl = k_lds(i), vl = v_lds(i);
+      const int kl = k_lds(i);
 #pragma unroll
       for (int c = 0; c < EB; ++c) *reinterpret_cast<i32x4*>(&kbuf[buf][kl + 16 * c]) = st.k[i][c];
+    }
+  };
+  auto store_v = [&](int buf, const Stage<EB, R>& st) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      const int vl = v_lds(i);
       if constexpr (PREC == kPrecFp8) {
         // widen 16 e4m3 codes to fp16 (exact) once per workgroup
         i32x4 lo, hi;
@@ -480,6 +501,10 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
         *reinterpret_cast<i32x4*>(&vbuf[buf][vl + 16]) = st.v[i][1];
       }
     }
+  };
+  auto store_stage = [&](int buf, const Stage<EB, R>& st) {
+    store_k(buf, st);
+    store_v(buf, st);
   };
 
   // Two staging register sets, each loaded two tiles ahead: while tile t is
@@ -503,20 +528,34 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
 
   // tile t+1 goes from its staging set to LDS and the set is refilled with
   // tile t+3 (both clamped to the range's last tile; past the end the copy
-  // lands in a buffer no later tile reads)
+  // lands in a buffer no later tile reads).  SB: K is stored and made visible
+  // first; V is stored after that barrier and made visible by a second one
+  // just before the tile's PV product (`mid`), so the tile's QK^T and softmax
+  // never wait for V's stores and widening.
   auto advance = [&](int64_t t, Stage<EB, R>& next) {
-    store_stage((int)((t + 1 - t0) & 1), next);
-    load_stage(clamp(t + 3), next);
-    __syncthreads();
+    const int buf = (int)((t + 1 - t0) & 1);
+    if constexpr (SB) {
+      store_k(buf, next);
+      __syncthreads();
+      store_v(buf, next);
+      load_stage(clamp(t + 3), next);
+    } else {
+      store_stage(buf, next);
+      load_stage(clamp(t + 3), next);
+      __syncthreads();
+    }
+  };
+  auto mid = [&]() {
+    if constexpr (SB) __syncthreads();
   };
   // tiles [t0, t_full) hold only valid keys; a partial tile can only be the
   // context's last one
   const int64_t t_full = (t1 * 64 > n) ? t1 - 1 : t1;
   const int rem_last = (int)(n - (t1 - 1) * 64);
   if (t0 < t_full)
-    attend_tile<PREC, QG, true, false>(ws, kbuf[0], vbuf[0], lg, col, hf, 64);
+    attend_tile<PREC, QG, true, false>(ws, kbuf[0], vbuf[0], lg, col, hf, 64, mid);
   else
-    attend_tile<PREC, QG, true, true>(ws, kbuf[0], vbuf[0], lg, col, hf, rem_last);
+    attend_tile<PREC, QG, true, true>(ws, kbuf[0], vbuf[0], lg, col, hf, rem_last, mid);
   advance(t0, sa);  // for a one-tile range this stages an unused copy of the last tile
   // tile t0+1+2i takes its successor from sb, tile t0+2+2i from sa.  The
   // pairs of tiles run in four quarters of falling issue priority (3 down to
@@ -532,20 +571,20 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
     set_wave_priority(3 - quarter);
     const int64_t t_q = t0 + 1 + 2 * (pairs * (quarter + 1) / 4);
     for (; t < t_q; t += 2) {
-      attend_tile<PREC, QG, false, false>(ws, kbuf[1], vbuf[1], lg, col, hf, 64);
+      attend_tile<PREC, QG, false, false>(ws, kbuf[1], vbuf[1], lg, col, hf, 64, mid);
       advance(t, sb);
-      attend_tile<PREC, QG, false, false>(ws, kbuf[0], vbuf[0], lg, col, hf, 64);
+      attend_tile<PREC, QG, false, false>(ws, kbuf[0], vbuf[0], lg, col, hf, 64, mid);
       advance(t + 1, sa);
     }
   }
   if (t < t_full) {
-    attend_tile<PREC, QG, false, false>(ws, kbuf[1], vbuf[1], lg, col, hf, 64);
+    attend_tile<PREC, QG, false, false>(ws, kbuf[1], vbuf[1], lg, col, hf, 64, mid);
     advance(t, sb);
     ++t;
   }
   if (t_full > t0 && t_full < t1) {
     const int cur = (int)((t_full - t0) & 1);
-    attend_tile<PREC, QG, false, true>(ws, kbuf[cur], vbuf[cur], lg, col, hf, rem_last);
+    attend_tile<PREC, QG, false, true>(ws, kbuf[cur], vbuf[cur], lg, col, hf, rem_last, mid);
   }
 
   // ---- epilogue
