@@ -174,7 +174,7 @@ sdm_icl_status sdm_icl_attn_query(sdm_icl_cache cache, const void* q, const void
  * the process ends).  The call allocates nothing: no hipMalloc, no
  * hipFree, no allocating library routine, no events (kernel timing is
  * skipped).  A query whose workspace (query_workspace_size) exceeds the
- * scratch array, e.g. 1,024 rows at 8 heads and 128 KV splits, returns
+ * scratch array, e.g. 1,024 rows at 8 heads and 96 KV splits, returns
  * SDM_ICL_E_INVALID with the sizes in the message; an offloaded cache
  * returns SDM_ICL_E_UNSUPPORTED (its streamed chunks need staging space).
  * Every call on one GPU shares that GPU's array, so calls that overlap on
@@ -328,7 +328,7 @@ sdm_icl_status sdm_icl_head_factors(int64_t n, const float* head_coef, int32_t h
 int32_t sdm_icl_select_precision(int64_t n, int32_t requested);
 
 /* KV split plan for n valid keys and bh_count = batch * heads on a device with
- * num_cus compute units: about 4 * num_cus / bh_count splits of at least 4
+ * num_cus compute units: about 3 * num_cus / bh_count splits of at least 4
  * key tiles each.  A pure function of (n, num_cus, bh_count), never of the
  * query count, so every query batch of a cache uses the same plan.  A cache
  * with per-batch lengths plans for the longest, max n_b; the splits past a

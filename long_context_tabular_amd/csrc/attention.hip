@@ -39,7 +39,8 @@
 //     Full tiles carry no masking code; the ragged last tile of the context
 //     is a separate instantiation.
 //   * O^T += V^T P^T with v_mfma_f32_32x32x16_f16; P is rounded to fp16
-//     (nearest even) and l is summed from the same rounded P (v_dot2).
+//     (nearest even) and l is summed from the same rounded P (4x4x4 MFMAs
+//     against ones, off the VALU).
 // Scheduling only (no result depends on it): split-KV launches run the row
 // blocks of one (split, head) back to back on one XCD so that they share its
 // K/V in that L2, and every wavefront lowers its issue priority by quarter of
@@ -63,7 +64,6 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef __fp16 h16x2 __attribute__((ext_vector_type(2)));
 
 // After a row's first tile, P is taken against a reference maximum that is
 // moved only when the 32 rounded P values one lane holds for that row in a
@@ -163,23 +163,23 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
   return fmaxf(lo, hi);
 }
 
-// fp32 sum of 16 fp16 P values (v_dot2 of each packed pair with (1, 1)).
+// fp32 sum of the lane's 16 fp16 P values, on the matrix pipe: each
+// v_mfma_f32_4x4x4_16b_f16 against an all-ones A operand gives every lane the
+// sum of its own four B halves (in all four of its output rows), accumulated
+// onto C.  Measured 0.6-0.8% faster than eight v_dot2c per 16 values on the
+// VALU, which is the attention kernels' bound.
 __device__ __forceinline__ float sum_p(const f16x8 (&p16)[2]) {
-  const h16x2 ones = {(__fp16)1.0f, (__fp16)1.0f};
-  float lsum = 0.f;
+  const f16x4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     const f16x8 pv = p16[ks];
-    const i32x4 words = __builtin_bit_cast(i32x4, pv);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // copy the element first: bit-casting a vector element directly
-      // reads element 0 with this compiler
-      const int word = words[i];
-      lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(h16x2, word), ones, lsum, false);
-    }
+    const f16x4 a = {pv[0], pv[1], pv[2], pv[3]};
+    const f16x4 b = {pv[4], pv[5], pv[6], pv[7]};
+    acc = __builtin_amdgcn_mfma_f32_4x4x4f16(ones, a, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_4x4x4f16(ones, b, acc, 0, 0, 0);
   }
-  return lsum;
+  return acc[0];
 }
 
 // P = fp16(exp2(s * c - m)) for the lane's 16 scores of one 32-key chunk;
@@ -745,9 +745,10 @@ hipError_t launch_attention(const AttnArgs& a, int prec, bool split, hipStream_t
   // wavefront (more MFMA work per LDS read and per softmax step); for FP16
   // the larger Q fragments push that kernel to the register limit, with a
   // few spills outside its tile loop, and it is still ~10% faster than one
-  // group.  FP8 split-KV calls take two groups too, with two-wavefront
-  // workgroups at most 128 rows so that one small query batch still fills
-  // the chip; FP16 split-KV calls keep one group (two measured slower).
+  // group.  Split-KV calls of at most 128 rows take one group per wavefront
+  // in four-wavefront workgroups (three wavefronts per SIMD over the split
+  // plan's three units per CU); FP8 calls of more rows take two groups;
+  // FP16 split-KV calls keep one group (two measured slower).
   const int64_t rows = split ? a.q_rows_valid : a.out_rows;
   auto go = [&](auto kern, int qt, int waves) {
     const dim3 grid((unsigned)((rows + qt - 1) / qt), (unsigned)(grid_splits > 0 ? grid_splits : a.splits),
@@ -756,7 +757,7 @@ hipError_t launch_attention(const AttnArgs& a, int prec, bool split, hipStream_t
   };
   if (prec == kPrecFp8) {
     if (split) {
-      if (a.q_rows_valid <= 128) go(attention_kernel<kPrecFp8, 2, true, 2>, 128, 2);
+      if (a.q_rows_valid <= 128) go(attention_kernel<kPrecFp8, 1, true, 4>, 128, 4);
       else go(attention_kernel<kPrecFp8, 2, true, 4>, 256, 4);
     } else {
       if (a.q_rows_valid <= 128) go(attention_kernel<kPrecFp8, 1, false, 4>, 128, 4);

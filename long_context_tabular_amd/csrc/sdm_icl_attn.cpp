@@ -56,10 +56,13 @@ namespace {
 
 constexpr uint64_t kMagic = 0x5344'4D49'434C'4131ull;  // "SDMICLA1"
 constexpr int64_t kFp8MinRows = 8192;
-// Split-KV plan: about kBlocksPerCu two-wavefront workgroups per CU over all
-// (b, h) of a small query batch, i.e. two wavefronts per SIMD, the occupancy
-// the register budget of the query kernel allows.
-constexpr int kBlocksPerCu = 4;
+// Split-KV plan: about kBlocksPerCu (split, head) units per CU over all (b, h).
+// A query batch of at most 128 rows runs one four-wavefront workgroup per
+// unit with one 32-row group per wavefront (131 VGPRs), i.e. three
+// wavefronts per SIMD, the occupancy its register budget allows (measured
+// 5% faster per call than four units per CU of two-wavefront, two-group
+// workgroups at two wavefronts per SIMD).
+constexpr int kBlocksPerCu = 3;
 constexpr int64_t kMinTilesPerSplit = 4;
 
 thread_local std::string g_error;

@@ -81,10 +81,11 @@ def test_split_plan_depends_on_n_cus_and_heads_only():
             assert kps % 64 == 0 and s >= 1
             assert (s - 1) * kps < n <= s * kps   # every split holds at least one valid key
             assert kps >= min(256, -(-n // 64) * 64)  # at least 4 tiles unless n is shorter
-    # 8 heads on 256 CUs: 128 splits x 8 heads = 4 two-wavefront workgroups per CU
-    assert B.sdm_icl_split_plan(524288, 256, 8) == (128, 4096)
-    assert B.sdm_icl_split_plan(523288, 256, 8) == (128, 4096)
-    assert B.sdm_icl_split_plan(524288, 256, 4) == (256, 2048)
+    # 8 heads on 256 CUs: 96 splits x 8 heads = 3 (split, head) units per CU,
+    # 86 key tiles per split
+    assert B.sdm_icl_split_plan(524288, 256, 8) == (96, 5504)
+    assert B.sdm_icl_split_plan(523288, 256, 8) == (96, 5504)
+    assert B.sdm_icl_split_plan(524288, 256, 4) == (191, 2752)
     for bad in ((0, 256, 8), (100, 0, 8), (100, 256, 0)):
         with pytest.raises(B.SdmIclError):
             B.sdm_icl_split_plan(*bad)

@@ -1,6 +1,6 @@
 """The split-KV combine across its chunk boundaries, through the C ABI.
 
-The split plan gives about 4 workgroups per CU over all (b, h) with at least
+The split plan gives about 3 (split, head) units per CU over all (b, h) with at least
 4 key tiles per split, so with 2 heads and one batch element n = 16,384 /
 16,640 / 32,768 / 33,000 / 70,000 rows give 64 / 65 / 128 / 129 / 274 splits
 on a 256-CU MI355X.  The combine takes up to 128 splits in one pass and more
