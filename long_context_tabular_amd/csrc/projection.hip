@@ -11,19 +11,23 @@
 // inference", Solution: the scaling is fused into the producer of q, with the
 // float32 length arithmetic and fp16 rounding boundaries of the eager path).
 //
-// Tiling: 128 x 128 output tiles, K in steps of 32; 4 wavefronts, each
-// 64 x 64 as 2 x 2 tiles of v_mfma_f32_32x32x16_f16.  Both operands are
-// K-contiguous, so the x and w tiles are staged into LDS the same way: global
-// loads that write LDS directly (no registers, no LDS store instructions)
-// into two stages, the next K step in flight while one is multiplied, one
-// barrier per step.  The kernel needs 100 VGPRs and 34 KB of LDS, so four
-// workgroups share a CU and cover each other's latency (measured faster than
-// deeper prefetch with fewer workgroups).  Staged rows are 64 bytes, unpadded; the
-// 16-byte chunk c of row r sits in slot c ^ ((r >> 2) & 3), which puts the 16
-// rows of one fragment read on 16 distinct bank groups (each lane fetches
-// the chunk that belongs in its fixed LDS slot).  Workgroups are mapped to
-// tiles so that the column tiles of one row tile run back to back on one XCD
-// and share the row tile in that XCD's L2.
+// Tiling: 256 x 128 output tiles, K in steps of 32; 4 wavefronts in 2 x 2,
+// each 128 x 64 as 4 x 2 tiles of v_mfma_f32_32x32x16_f16 (43 FLOP per byte
+// of fragment reads, against 32 for 64 x 64 wavefront tiles).  Both operands
+// are K-contiguous, so the x and w tiles are staged into LDS the same way:
+// global loads that write LDS directly (no registers, no LDS store
+// instructions) into two stages, the next K step in flight while one is
+// multiplied, one barrier per step.  The kernel needs 173 VGPRs and 48 KB of
+// LDS (74 KB with the output tile), two workgroups per CU.  Staged rows are
+// 64 bytes, unpadded; the 16-byte chunk c of row r sits in slot
+// c ^ ((r >> 2) & 3), which puts the 16 rows of one fragment read on 16
+// distinct bank groups (each lane fetches the chunk that belongs in its fixed
+// LDS slot).  Workgroups are mapped to tiles so that the column tiles of one
+// row tile run back to back on one XCD and share the row tile in that XCD's
+// L2.  The output tile is assembled in LDS and written as 16-byte row
+// segments with non-temporal stores (1.5 GB of outputs at the 524,288-row
+// shape that nothing reads back soon; keeping them out of L2 leaves it to the
+// x tiles).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -37,14 +41,17 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 128, kBN = 128, kBK = 32;
+constexpr int kBM = 256, kBN = 128, kBK = 32;
+constexpr int kWM = 128, kWN = 64;              // output tile of one wavefront (2 x 2 wavefronts)
 constexpr int kStages = 2;                      // LDS stages (K steps in flight: kStages - 1)
 constexpr int kRowB = kBK * 2;                  // bytes per staged row (64, unpadded)
-constexpr int kStageB = (kBM + kBN) * kRowB;    // 16 KB: the x tile, then the w tile
-constexpr int kCRow = 136;  // LDS halves per row of the output tile (128 + 8 pad)
+constexpr int kStageB = (kBM + kBN) * kRowB;    // 24 KB: the x tile, then the w tile
+constexpr int kXBlocks = kBM / 16 / 4, kWBlocks = kBN / 16 / 4;  // 16-row blocks per wave and step
+constexpr int kLoads = kXBlocks + kWBlocks;     // loads per wave and step
+constexpr int kCRow = kBN + 8;  // LDS halves per row of the output tile (8 pad)
 constexpr int kSmemB = kStages * kStageB > kBM * kCRow * 2 ? kStages * kStageB : kBM * kCRow * 2;
 static_assert(kBM * kCRow * 2 <= kSmemB, "output tile must fit in the operand stages");
-static_assert(kBM == 128 && kBN == 128 && kBK == 32, "the load mapping covers 16 rows per wave instruction");
+static_assert(kBK == 32, "the load mapping covers 16 rows of 64 bytes per wave instruction");
 
 // LDS slot of the 16-byte chunk c (of 4) of staged row r; an involution in c
 __device__ __forceinline__ int chunk_slot(int r, int c) { return c ^ ((r >> 2) & 3); }
@@ -63,7 +70,7 @@ __global__ __launch_bounds__(256, 2) void qkv_project_kernel(
   __shared__ float gate_u[kBM][2];  // gate factors of the tile's rows for its (at most) two heads
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv >> 1, wn = wv & 1;
+  const int wm = wv >> 1, wn = wv & 1;   // the wave's 128-row half and 64-column half
   // XCD-aware tile order: workgroups are handed to the 8 XCDs round-robin, so
   // workgroup L runs on XCD L % 8.  XCD j takes the row tiles j, j + 8, ...
   // and runs all column tiles of one row tile back to back, which then share
@@ -86,9 +93,9 @@ __global__ __launch_bounds__(256, 2) void qkv_project_kernel(
   const int64_t m0 = rt * kBM;
 
   // Step kt's x and w tiles go to stage kt % kStages.  Wave wv, instruction i
-  // fills 16-row block 2 wv + i of each tile: lane l lands in row
-  // 16 (2 wv + i) + l / 4, slot l % 4, so it fetches that row's chunk
-  // chunk_slot(row, l % 4).  Rows past the end re-read the last row (their
+  // fills 16-row block kXBlocks wv + i of the x tile (kWBlocks wv + i of the
+  // w tile): lane l lands in row 16 blk + l / 4, slot l % 4, so it fetches
+  // that row's chunk chunk_slot(row, l % 4).  Rows past the end re-read the last row (their
   // outputs are never stored), and steps past the last re-read it into a
   // stage no later step reads, so that every wave always has the same number
   // of loads in flight.
@@ -97,33 +104,29 @@ __global__ __launch_bounds__(256, 2) void qkv_project_kernel(
     const int k0 = (kt < nk ? kt : nk - 1) * kBK;
     unsigned char* st = smem + (kt % kStages) * kStageB;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int blk = 2 * wv + i;
+    for (int i = 0; i < kXBlocks; ++i) {
+      const int blk = kXBlocks * wv + i;
       const int r = 16 * blk + (lane >> 2);
       const int c = chunk_slot(r, lane & 3);
       const int64_t m = m0 + r;
-      const int n = n0 + r;
       __builtin_amdgcn_global_load_lds(x + (m < M ? m : M - 1) * K + k0 + c * 8, st + blk * 1024, 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kWBlocks; ++i) {
+      const int blk = kWBlocks * wv + i;
+      const int r = 16 * blk + (lane >> 2);
+      const int c = chunk_slot(r, lane & 3);
+      const int n = n0 + r;
       __builtin_amdgcn_global_load_lds(w + (int64_t)(n < N ? n : N - 1) * K + k0 + c * 8,
                                        st + kBM * kRowB + blk * 1024, 16, 0, 0);
     }
   };
 
-  if constexpr (MODE == kScaleGated) {
-    if (n0 < HD) {
-      // one gate factor per (row, head) of the tile, computed once
-      const int r = tid >> 1, hh = tid & 1;
-      const int head = n0 / 64 + hh;
-      const int64_t m = m0 + r;
-      gate_u[r][hh] = (m < M && head < H) ? gate_factor(gate[m * H + head]) : 1.0f;
-    }
-  }
-
-  f32x16 acc[2][2];
+  f32x16 acc[kWM / 32][kWN / 32];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kWM / 32; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+    for (int j = 0; j < kWN / 32; ++j) acc[i][j] = f32x16{};
 
   // Step kt: wait for its own loads (issued kStages - 1 steps earlier; the 4
   // loads of each later step may still be in flight), then a barrier that
@@ -131,11 +134,25 @@ __global__ __launch_bounds__(256, 2) void qkv_project_kernel(
   // from, which step kt + kStages - 1 then refills.
 #pragma unroll
   for (int d = 0; d < kStages - 1; ++d) load(d);
+  // the gate factors are computed while the first steps' loads are in flight
+  if constexpr (MODE == kScaleGated) {
+    if (n0 < HD) {
+      // one gate factor per (row, head) of the tile, computed once
+#pragma unroll
+      for (int p = 0; p < kBM * 2 / 256; ++p) {
+        const int e = tid + 256 * p, r = e >> 1, hh = e & 1;
+        const int head = n0 / 64 + hh;
+        const int64_t m = m0 + r;
+        gate_u[r][hh] = (m < M && head < H) ? gate_factor(gate[m * H + head]) : 1.0f;
+      }
+    }
+  }
+
   for (int kt = 0; kt < nk; ++kt) {
     // an explicit wait and a bare s_barrier: __syncthreads() adds a fence
     // that waits for every load in flight, which with more than two stages
     // would drain the prefetch
-    SDM_WAIT_VMCNT(4 * (kStages - 2));
+    SDM_WAIT_VMCNT(kLoads * (kStages - 2));
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");  // the LDS stage was written behind the compiler's back
     load(kt + kStages - 1);
@@ -144,18 +161,22 @@ __global__ __launch_bounds__(256, 2) void qkv_project_kernel(
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int c = 2 * kk + (lane >> 5);
-      f16x8 a[2], b[2];
+      f16x8 a[kWM / 32], b[kWN / 32];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int ra = wm * 64 + t * 32 + (lane & 31);
-        const int rb = wn * 64 + t * 32 + (lane & 31);
+      for (int t = 0; t < kWM / 32; ++t) {
+        const int ra = wm * kWM + t * 32 + (lane & 31);
         a[t] = *reinterpret_cast<const f16x8*>(at + ra * kRowB + chunk_slot(ra, c) * 16);
+      }
+#pragma unroll
+      for (int t = 0; t < kWN / 32; ++t) {
+        const int rb = wn * kWN + t * 32 + (lane & 31);
         b[t] = *reinterpret_cast<const f16x8*>(bt + rb * kRowB + chunk_slot(rb, c) * 16);
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < kWM / 32; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < kWN / 32; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
   }
   // the loads past the last step must land before the output tile reuses the
@@ -170,18 +191,18 @@ __global__ __launch_bounds__(256, 2) void qkv_project_kernel(
   // barrier), then written out as 16-byte row segments.
   _Float16* const ct = reinterpret_cast<_Float16*>(smem);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int cc = wn * 64 + j * 32 + (lane & 31);
+  for (int j = 0; j < kWN / 32; ++j) {
+    const int cc = wn * kWN + j * 32 + (lane & 31);
     const int n = n0 + cc;
     const int nn = n < N ? n : N - 1;
     const int t = nn / HD, c = nn - t * HD;
     const float bn = bias ? (float)bias[nn] : 0.f;
     const float kf = (float)__builtin_bit_cast(_Float16, kh.bits[(c >> 6) < kMaxHeads ? (c >> 6) : 0]);
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kWM / 32; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int rr = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int rr = wm * kWM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         _Float16 y = (_Float16)(acc[i][j][r] + bn);
         if (t == 0) {
           float u = 1.0f;
@@ -192,7 +213,7 @@ __global__ __launch_bounds__(256, 2) void qkv_project_kernel(
       }
   }
   __syncthreads();
-  // 128 rows x 16 segments of 8 halves; a segment never straddles two
+  // kBM rows x 16 segments of 8 halves; a segment never straddles two
   // tensors (H*64 is a multiple of 8)
 #pragma unroll
   for (int p = 0; p < (kBM * kBN / 8) / 256; ++p) {
@@ -202,7 +223,8 @@ __global__ __launch_bounds__(256, 2) void qkv_project_kernel(
     if (m >= M || n >= N) continue;
     const int t = n / HD, c = n - t * HD;
     _Float16* out = t == 0 ? q_out : (t == 1 ? k_out : v_out);
-    *reinterpret_cast<i32x4*>(out + m * HD + c) = *reinterpret_cast<const i32x4*>(&ct[row * kCRow + c8 * 8]);
+    __builtin_nontemporal_store(*reinterpret_cast<const i32x4*>(&ct[row * kCRow + c8 * 8]),
+                                reinterpret_cast<i32x4*>(out + m * HD + c));
   }
 }
 

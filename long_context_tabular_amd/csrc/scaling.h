@@ -26,10 +26,19 @@ __device__ inline _Float16 f64_to_f16(double d) {
   return (_Float16)f;
 }
 
-// fp16(1 + fp16(tanh g)) as a float; tanh is evaluated in double so the fp16
-// result is the correctly rounded one.
+// fp16(1 + fp16(tanh g)) as a float, with fp16(tanh g) correctly rounded.
+// Fast path: the float32 tanhf is accurate to a few float32 ulps, far inside
+// 2^-19 relative, so when t * (1 - 2^-19) and t * (1 + 2^-19) round to the
+// same fp16 value, that value is the correctly rounded fp16 of tanh g.
+// Otherwise (tanh g lies next to an fp16 rounding boundary) tanh is taken in
+// double.  Exhaustively equal, over every finite fp16 gate, to rounding the
+// double tanh.
 __device__ inline float gate_factor(_Float16 g) {
-  const _Float16 t = f64_to_f16(tanh((double)g));
+  const float t32 = tanhf((float)g);
+  _Float16 t = (_Float16)t32;
+  const _Float16 lo = (_Float16)(t32 * (1.0f - 0x1p-19f));
+  const _Float16 hi = (_Float16)(t32 * (1.0f + 0x1p-19f));
+  if (lo != t || hi != t) t = f64_to_f16(tanh((double)g));
   return (float)(_Float16)(1.0f + (float)t);
 }
 
