@@ -52,6 +52,9 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "internal.h"
 
 namespace sdm {
@@ -128,6 +131,24 @@ struct Ops<kPrecFp16> {
 };
 
 constexpr int kVRow = 144;  // LDS bytes per d-row of the fp16 V^T tile (128 + 16 pad)
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>), in order.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Staging register sets (tiles loaded ahead of their LDS store).  Two: with
+// four or six for the FP8 split-KV kernels, which stream their K/V from HBM,
+// the 128-row cached query kernel measured the same (139-142 us), so the
+// time it loses to HBM streaming (122 us with its K/V held in L2) is not
+// load latency.
+template <int PREC, bool SPLIT>
+constexpr int stage_sets() { return 2; }
 
 // Stage each tile's K and V behind separate barriers (see advance()): the
 // tile's QK^T and softmax start once K is in LDS, and V's stores (and FP8
@@ -338,7 +359,8 @@ __device__ __forceinline__ void set_wave_priority(int p) {
   }
 }
 
-template <int PREC, int QG, bool SPLIT, int W, bool SB = split_barrier<PREC, SPLIT>()>
+template <int PREC, int QG, bool SPLIT, int W, bool SB = split_barrier<PREC, SPLIT>(),
+          int NS = stage_sets<PREC, SPLIT>()>
 __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
   typedef Ops<PREC> O;
   constexpr int EB = O::EB;
@@ -507,10 +529,10 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
     store_v(buf, st);
   };
 
-  // Two staging register sets, each loaded two tiles ahead: while tile t is
-  // processed, the loads of tiles t+1 and t+2 are in flight.  Tile t+1 is
-  // written to the other LDS buffers at the end of tile t (one barrier per
-  // tile); the set it came from is then reloaded with tile t+3.
+  // NS staging register sets, each loaded NS tiles ahead: while tile t is
+  // processed, the loads of tiles t+1 .. t+NS are in flight.  Tile t+1 is
+  // written to the other LDS buffers at the end of tile t; the set it came
+  // from is then reloaded with tile t+1+NS.
   //
   // Every load is issued on every path (past the end of the split they
   // re-read its last tile), so the number of loads in flight is the same
@@ -519,15 +541,17 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
   set_wave_priority(3);
   const int64_t t_last = t1 - 1;
   auto clamp = [&](int64_t t) { return t < t_last ? t : t_last; };
-  Stage<EB, R> sa, sb;
-  load_stage(t0, sa);
-  store_stage(0, sa);
-  load_stage(clamp(t0 + 1), sa);
-  load_stage(clamp(t0 + 2), sb);
+  // NS staging register sets: set i first takes tile t0 + 1 + i, so a tile's
+  // loads are issued NS tiles before it is stored to LDS.
+  Stage<EB, R> st[NS];
+  load_stage(t0, st[0]);
+  store_stage(0, st[0]);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) load_stage(clamp(t0 + 1 + i), st[i]);
   __syncthreads();
 
   // tile t+1 goes from its staging set to LDS and the set is refilled with
-  // tile t+3 (both clamped to the range's last tile; past the end the copy
+  // tile t+1+NS (both clamped to the range's last tile; past the end the copy
   // lands in a buffer no later tile reads).  SB: K is stored and made visible
   // first; V is stored after that barrier and made visible by a second one
   // just before the tile's PV product (`mid`), so the tile's QK^T and softmax
@@ -538,10 +562,10 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
       store_k(buf, next);
       __syncthreads();
       store_v(buf, next);
-      load_stage(clamp(t + 3), next);
+      load_stage(clamp(t + 1 + NS), next);
     } else {
       store_stage(buf, next);
-      load_stage(clamp(t + 3), next);
+      load_stage(clamp(t + 1 + NS), next);
       __syncthreads();
     }
   };
@@ -556,32 +580,36 @@ __global__ __launch_bounds__(W * 64, 2) void attention_kernel(AttnArgs a) {
     attend_tile<PREC, QG, true, false>(ws, kbuf[0], vbuf[0], lg, col, hf, 64, mid);
   else
     attend_tile<PREC, QG, true, true>(ws, kbuf[0], vbuf[0], lg, col, hf, rem_last, mid);
-  advance(t0, sa);  // for a one-tile range this stages an unused copy of the last tile
-  // tile t0+1+2i takes its successor from sb, tile t0+2+2i from sa.  The
-  // pairs of tiles run in four quarters of falling issue priority (3 down to
-  // 0): among the wavefronts sharing a SIMD the hardware favours the oldest,
-  // so without this a wavefront that started a moment later falls behind and
-  // finishes its last tiles alone, with no partner to overlap its MFMAs and
-  // its softmax; a wavefront that lags now keeps precedence until it reaches
-  // the next quarter.  Priority only orders issue; no result depends on it.
+  advance(t0, st[0]);  // for a one-tile range this stages an unused copy of the last tile
+  // Tile t (> t0) is in LDS buffer (t - t0) & 1 and its successor in staging
+  // set (t - t0) % NS; the loop takes NS tiles at a time from t0 + 1, so both
+  // indices are compile-time constants in its body.  The groups of tiles run
+  // in four quarters of falling issue priority (3 down to 0): among the
+  // wavefronts sharing a SIMD the hardware favours the oldest, so without
+  // this a wavefront that started a moment later falls behind and finishes
+  // its last tiles alone, with no partner to overlap its MFMAs and its
+  // softmax; a wavefront that lags now keeps precedence until it reaches the
+  // next quarter.  Priority only orders issue; no result depends on it.
+  auto full_tile = [&](int64_t t, auto J) __attribute__((always_inline)) {
+    constexpr int j = decltype(J)::value;   // t - t0 = 1 + j (mod NS)
+    constexpr int b = (1 + j) & 1;
+    attend_tile<PREC, QG, false, false>(ws, kbuf[b], vbuf[b], lg, col, hf, 64, mid);
+    advance(t, st[(1 + j) % NS]);
+  };
   int64_t t = t0 + 1;
-  const int64_t pairs = t_full > t ? (t_full - t) / 2 : 0;
+  const int64_t groups = t_full > t ? (t_full - t) / NS : 0;
 #pragma unroll 1
   for (int quarter = 0; quarter < 4; ++quarter) {
     set_wave_priority(3 - quarter);
-    const int64_t t_q = t0 + 1 + 2 * (pairs * (quarter + 1) / 4);
-    for (; t < t_q; t += 2) {
-      attend_tile<PREC, QG, false, false>(ws, kbuf[1], vbuf[1], lg, col, hf, 64, mid);
-      advance(t, sb);
-      attend_tile<PREC, QG, false, false>(ws, kbuf[0], vbuf[0], lg, col, hf, 64, mid);
-      advance(t + 1, sa);
-    }
+    const int64_t t_q = t0 + 1 + NS * (groups * (quarter + 1) / 4);
+    for (; t < t_q; t += NS)
+      static_for<NS>([&](auto J) __attribute__((always_inline)) { full_tile(t + decltype(J)::value, J); });
   }
-  if (t < t_full) {
-    attend_tile<PREC, QG, false, false>(ws, kbuf[1], vbuf[1], lg, col, hf, 64, mid);
-    advance(t, sb);
-    ++t;
-  }
+  // fewer than NS full tiles remain (the same for every wavefront of the
+  // workgroup, so every wavefront passes the same barriers)
+  static_for<NS - 1>([&](auto J) __attribute__((always_inline)) {
+    if (t + decltype(J)::value < t_full) full_tile(t + decltype(J)::value, J);
+  });
   if (t_full > t0 && t_full < t1) {
     const int cur = (int)((t_full - t0) & 1);
     attend_tile<PREC, QG, false, true>(ws, kbuf[cur], vbuf[cur], lg, col, hf, rem_last, mid);
