@@ -17,17 +17,21 @@
 // are K-contiguous, so the x and w tiles are staged into LDS the same way:
 // global loads that write LDS directly (no registers, no LDS store
 // instructions) into two stages, the next K step in flight while one is
-// multiplied, one barrier per step.  The kernel needs 173 VGPRs and 48 KB of
-// LDS (74 KB with the output tile), two workgroups per CU.  Staged rows are
+// multiplied, one barrier per step.  The kernel is held to 168 VGPRs and
+// 48 KB of LDS (50 KB with the gate factors), so that three workgroups share
+// a CU and one's epilogue runs beside the others' K loops.  Staged rows are
 // 64 bytes, unpadded; the 16-byte chunk c of row r sits in slot
 // c ^ ((r >> 2) & 3), which puts the 16 rows of one fragment read on 16
 // distinct bank groups (each lane fetches the chunk that belongs in its fixed
 // LDS slot).  Workgroups are mapped to tiles so that the column tiles of one
 // row tile run back to back on one XCD and share the row tile in that XCD's
-// L2.  The output tile is assembled in LDS and written as 16-byte row
-// segments with non-temporal stores (1.5 GB of outputs at the 524,288-row
-// shape that nothing reads back soon; keeping them out of L2 leaves it to the
-// x tiles).
+// L2.  The output tile is assembled in LDS one 128-row half at a time (each
+// half fits in the operand stages) and written as 16-byte row segments with
+// non-temporal stores (1.5 GB of outputs at the 524,288-row shape that
+// nothing reads back soon; keeping them out of L2 leaves it to the x tiles).
+// GatedLogScale multiplies by the gate factor in that store pass, where a
+// thread's 8 values share one (row, head): fp16(fp16(y k_h) u) in the same
+// two roundings as the separate pass.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -49,8 +53,8 @@ constexpr int kStageB = (kBM + kBN) * kRowB;    // 24 KB: the x tile, then the w
 constexpr int kXBlocks = kBM / 16 / 4, kWBlocks = kBN / 16 / 4;  // 16-row blocks per wave and step
 constexpr int kLoads = kXBlocks + kWBlocks;     // loads per wave and step
 constexpr int kCRow = kBN + 8;  // LDS halves per row of the output tile (8 pad)
-constexpr int kSmemB = kStages * kStageB > kBM * kCRow * 2 ? kStages * kStageB : kBM * kCRow * 2;
-static_assert(kBM * kCRow * 2 <= kSmemB, "output tile must fit in the operand stages");
+constexpr int kSmemB = kStages * kStageB > kWM * kCRow * 2 ? kStages * kStageB : kWM * kCRow * 2;
+static_assert(kWM * kCRow * 2 <= kSmemB, "half the output tile must fit in the operand stages");
 static_assert(kBK == 32, "the load mapping covers 16 rows of 64 bytes per wave instruction");
 
 // LDS slot of the 16-byte chunk c (of 4) of staged row r; an involution in c
@@ -62,7 +66,7 @@ __device__ __forceinline__ int chunk_slot(int r, int c) { return c ^ ((r >> 2) &
 #define SDM_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
 
 template <int MODE>
-__global__ __launch_bounds__(256, 2) void qkv_project_kernel(
+__global__ __launch_bounds__(256, 3) void qkv_project_kernel(
     const _Float16* __restrict__ x, const _Float16* __restrict__ w, const _Float16* __restrict__ bias,
     int64_t M, int N, int K, int HD, int H, HeadFactors kh, const _Float16* __restrict__ gate,
     _Float16* __restrict__ q_out, _Float16* __restrict__ k_out, _Float16* __restrict__ v_out) {
@@ -186,45 +190,55 @@ __global__ __launch_bounds__(256, 2) void qkv_project_kernel(
   asm volatile("" ::: "memory");
 
   // ---- epilogue.  Each lane holds column wn*64 + j*32 + lane%32 of 16 rows
-  // per tile: bias, one fp16 rounding and the Q scaling are applied there and
-  // the tile is assembled in LDS (the operand stages are free after the last
-  // barrier), then written out as 16-byte row segments.
+  // per tile: bias, one fp16 rounding and the head factor of the Q columns
+  // are applied there; the two wavefronts of one 128-row half assemble it in
+  // LDS (the operand stages are free after the last barrier), and all four
+  // write it out as 16-byte row segments, GatedLogScale's gate factor applied
+  // on the way.
   _Float16* const ct = reinterpret_cast<_Float16*>(smem);
+  constexpr int kFirst = MODE == kScaleGated ? kScaleLog : MODE;  // scaling before the gate
+  for (int half = 0; half < 2; ++half) {
+    if (wm == half) {
 #pragma unroll
-  for (int j = 0; j < kWN / 32; ++j) {
-    const int cc = wn * kWN + j * 32 + (lane & 31);
-    const int n = n0 + cc;
-    const int nn = n < N ? n : N - 1;
-    const int t = nn / HD, c = nn - t * HD;
-    const float bn = bias ? (float)bias[nn] : 0.f;
-    const float kf = (float)__builtin_bit_cast(_Float16, kh.bits[(c >> 6) < kMaxHeads ? (c >> 6) : 0]);
+      for (int j = 0; j < kWN / 32; ++j) {
+        const int cc = wn * kWN + j * 32 + (lane & 31);
+        const int n = n0 + cc;
+        const int nn = n < N ? n : N - 1;
+        const int t = nn / HD, c = nn - t * HD;
+        const float bn = bias ? (float)bias[nn] : 0.f;
+        const float kf = (float)__builtin_bit_cast(_Float16, kh.bits[(c >> 6) < kMaxHeads ? (c >> 6) : 0]);
 #pragma unroll
-    for (int i = 0; i < kWM / 32; ++i)
+        for (int i = 0; i < kWM / 32; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rr = wm * kWM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        _Float16 y = (_Float16)(acc[i][j][r] + bn);
-        if (t == 0) {
-          float u = 1.0f;
-          if constexpr (MODE == kScaleGated) u = gate_u[rr][(c >> 6) - n0 / 64];
-          y = scale_elem<MODE>(y, kf, u);
-        }
-        ct[rr * kCRow + cc] = y;
+          for (int r = 0; r < 16; ++r) {
+            const int rl = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            _Float16 y = (_Float16)(acc[i][j][r] + bn);
+            if (t == 0) y = scale_elem<kFirst>(y, kf, 1.0f);
+            ct[rl * kCRow + cc] = y;
+          }
       }
-  }
-  __syncthreads();
-  // kBM rows x 16 segments of 8 halves; a segment never straddles two
-  // tensors (H*64 is a multiple of 8)
+    }
+    __syncthreads();
 #pragma unroll
-  for (int p = 0; p < (kBM * kBN / 8) / 256; ++p) {
-    const int q = tid + 256 * p, row = q >> 4, c8 = q & 15;
-    const int64_t m = m0 + row;
-    const int n = n0 + c8 * 8;
-    if (m >= M || n >= N) continue;
-    const int t = n / HD, c = n - t * HD;
-    _Float16* out = t == 0 ? q_out : (t == 1 ? k_out : v_out);
-    __builtin_nontemporal_store(*reinterpret_cast<const i32x4*>(&ct[row * kCRow + c8 * 8]),
-                                reinterpret_cast<i32x4*>(out + m * HD + c));
+    for (int p = 0; p < (kWM * kBN / 8) / 256; ++p) {
+      const int q = tid + 256 * p, row = q >> 4, c8 = q & 15;
+      const int64_t m = m0 + half * kWM + row;
+      const int n = n0 + c8 * 8;
+      if (m < M && n < N) {
+        const int t = n / HD, c = n - t * HD;
+        _Float16* out = t == 0 ? q_out : (t == 1 ? k_out : v_out);
+        f16x8 y = *reinterpret_cast<const f16x8*>(&ct[row * kCRow + c8 * 8]);
+        if constexpr (MODE == kScaleGated) {
+          if (t == 0) {
+            const float u = gate_u[half * kWM + row][(c >> 6) - n0 / 64];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) y[e] = (_Float16)((float)y[e] * u);
+          }
+        }
+        __builtin_nontemporal_store(__builtin_bit_cast(i32x4, y), reinterpret_cast<i32x4*>(out + m * HD + c));
+      }
+    }
+    __syncthreads();
   }
 }
 

@@ -24,9 +24,12 @@ MAGIC = b"__CLANG_OFFLOAD_BUNDLE__"
 
 # (kernel name pattern, largest private segment in bytes): the FP16 two-group
 # context kernel sits at the register limit and spills 28 registers outside
-# its tile loop; every other kernel keeps everything in registers
+# its tile loop, and the GatedLogScale projection (at the 168-register budget
+# of three workgroups per CU) a handful around its K loop; every other kernel
+# keeps everything in registers
 LIMITS = [
     (r"attention_kernelILi0ELi2ELb0E", 128),
+    (r"qkv_project_kernelILi2E", 32),
     (r"attention_kernel", 0),
     (r"qkv_project_kernel", 0),
     (r"combine_kernel", 0),
