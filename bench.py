@@ -18,6 +18,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -40,13 +41,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _code_only(text: str, py: bool) -> str:
+    """The source with its comments and blank lines removed, so that a change
+    to a comment does not invalidate a measurement of the same code."""
+    if py:
+        text = re.sub(r"(?m)^\s*#.*$", "", text)
+    else:
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash() -> str:
     """sha256 (first 16 hex digits) of the attention kernels' sources and of
-    build_lib.py, which holds their compiler flags."""
+    build_lib.py, which holds their compiler flags, comments excluded."""
     h = hashlib.sha256()
     for f in ("csrc/attention.hip", "csrc/prep.hip", "csrc/scaling.h", "build_lib.py"):
-        with open(os.path.join(ROOT, "long_context_tabular_amd", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "long_context_tabular_amd", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read(), f.endswith(".py")).encode())
     return h.hexdigest()[:16]
 
 

@@ -153,7 +153,7 @@ constexpr int stage_sets() { return 2; }
 // Stage each tile's K and V behind separate barriers (see advance()): the
 // tile's QK^T and softmax start once K is in LDS, and V's stores (and FP8
 // widening) go on in their shadow.  Measured against one barrier per tile on
-// one box: the FP16 16K context pass 1.8% and the 128-row cached query kernel
+// one MI355X: the FP16 16K context pass 1.8% and the 128-row cached query kernel
 // 2% faster, the FP8 context passes 1.2% (512K) to 2.8% (128K) slower, so the
 // FP8 context kernel keeps the single barrier.
 template <int PREC, bool SPLIT>

@@ -50,6 +50,22 @@ def test_counter_traffic_only_for_matching_sources(tmp_path, monkeypatch):
     assert bench.counter_traffic("context") is None
 
 
+def test_comment_changes_keep_the_record_and_code_changes_retire_it(tmp_path, monkeypatch):
+    src = "// staging\nint f() { return 1; }  // one\n/* block\n comment */\n"
+    pkg = _tree(tmp_path, src)
+    (pkg / "build_lib.py").write_text("# flags\nFLAGS = ['-O3']\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    h0 = bench.kernel_source_hash()
+    (pkg / "csrc" / "attention.hip").write_text("// reworded\n\nint f() { return 1; }  // two\n")
+    (pkg / "build_lib.py").write_text("# other words\nFLAGS = ['-O3']\n")
+    assert bench.kernel_source_hash() == h0
+    (pkg / "csrc" / "attention.hip").write_text("int f() { return 2; }\n")
+    assert bench.kernel_source_hash() != h0
+    (pkg / "csrc" / "attention.hip").write_text(src)
+    (pkg / "build_lib.py").write_text("FLAGS = ['-O2']\n")
+    assert bench.kernel_source_hash() != h0
+
+
 def test_committed_traffic_record_is_well_formed():
     path = os.path.join(ROOT, "profiles", "traffic_context_model512k.txt")
     if not os.path.exists(path):
