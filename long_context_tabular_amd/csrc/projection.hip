@@ -132,8 +132,8 @@ __global__ __launch_bounds__(256, 3) void qkv_project_kernel(
 #pragma unroll
     for (int j = 0; j < kWN / 32; ++j) acc[i][j] = f32x16{};
 
-  // Step kt: wait for its own loads (issued kStages - 1 steps earlier; the 4
-  // loads of each later step may still be in flight), then a barrier that
+  // Step kt: wait for its own loads (issued kStages - 1 steps earlier; the
+  // kLoads loads of each later step may still be in flight), then a barrier that
   // makes every wave's loads visible and frees the stage step kt - 1 was read
   // from, which step kt + kStages - 1 then refills.
 #pragma unroll
