@@ -350,13 +350,28 @@ def bench_projection(B, w, reps: int = 21, warmup: int = 10):
         b.record()
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in evs)[reps // 2]
+    # reference point, not part of the path: torch's library GEMM (hipBLASLt)
+    # on the same shape, fp16 in and out with the bias and without the scaling
+    x2, y2 = x.view(w.n_pad, E), torch.empty((w.n_pad, 3 * E), dtype=torch.float16, device="cuda")
+    lib = lambda: torch.addmm(bias, x2, wt.t(), out=y2)
+    for _ in range(warmup):
+        lib()
+    torch.cuda.synchronize()
+    for a, b in evs:
+        a.record()
+        lib()
+        b.record()
+    torch.cuda.synchronize()
+    lib_ms = sorted(a.elapsed_time(b) for a, b in evs)[reps // 2]
     flops = 2.0 * w.n_pad * 3 * E * E
     hbm = (w.n_pad * E + 3 * E * E + 3 * w.n_pad * E) * 2
     return {"rows": w.n_pad, "in_features": E, "out_features": 3 * E, "ms": round(ms, 4),
             "TFLOP_per_s": round(flops / (ms * 1e-3) / 1e12, 1),
             "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_FP16_TFLOPS, 4),
             "GB_per_s": round(hbm / (ms * 1e-3) / 1e9, 1),
-            "hbm_frac": round(hbm / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+            "hbm_frac": round(hbm / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "library_gemm_ms": round(lib_ms, 4),
+            "library_gemm": "torch.addmm (hipBLASLt), same shape, fp16, bias, no query scaling"}
 
 
 def cpu_baseline(gen, x, w, sample_rows: int):
