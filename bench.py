@@ -174,13 +174,14 @@ def bench_model_call(B, gen, w, steps, warmup):
     gq = dev(x.gate_query) if gated else None
     out = torch.empty_like(q)
     qout = torch.empty_like(qq)
-    c = B.sdm_icl_attn_fit(q, k, v, w.n_valid, w.scale_mode, w.precision, coef, gate, None)
+    lengths = w.length_list() if w.lengths else w.n_valid
+    c = B.sdm_icl_attn_fit(q, k, v, lengths, w.scale_mode, w.precision, coef, gate, None)
     info = c.info()
     ws = torch.empty(B.sdm_icl_attn_query_workspace_size(c, w.n_query), dtype=torch.uint8, device="cuda")
     c.release()
 
     def step():
-        cache = B.sdm_icl_attn_fit(q, k, v, w.n_valid, w.scale_mode, w.precision, coef, gate, out)
+        cache = B.sdm_icl_attn_fit(q, k, v, lengths, w.scale_mode, w.precision, coef, gate, out)
         B.sdm_icl_attn_query(cache, qq, gq, out=qout, workspace=ws)
         cache.release()
 
@@ -205,7 +206,8 @@ def bench_model_call(B, gen, w, steps, warmup):
 
 
 def bench_other_workload(B, gen, name, steps, warm_ms=60.0):
-    """A model call of another workload (the 128K FP8 and the 16K FP16 ones):
+    """A model call of another workload (the 128K FP8, the 16K FP16 and the
+    ragged 128K + 64K FP8 ones; a ragged call counts each element at its own length):
     warm-up calls adding up to about warm_ms of GPU work first (a few
     milliseconds leave the clocks below their steady state), then `steps`
     timed calls; the context kernel's time from the in-stream events."""
@@ -215,16 +217,19 @@ def bench_other_workload(B, gen, name, steps, warm_ms=60.0):
     warm = max(3, int(math.ceil(warm_ms / max(sec1 * 1e3, 1e-3))))
     _, info, sec, t = bench_model_call(B, gen, w, steps, warm)
     n, H, D, R = w.n_valid, w.heads, w.head_dim, w.n_query
-    ctx_flops = 4.0 * n * n * D * H
+    ns = w.length_list()                      # valid rows of each batch element
+    ctx_flops = 4.0 * sum(m * m for m in ns) * D * H
+    q_flops = 4.0 * R * sum(ns) * D * H
     ctx_ms = t["context"][0] / max(t["context"][1], 1)
     achieved = ctx_flops / (ctx_ms * 1e-3) / 1e12
     fp8 = info["precision"] == 1
     peak = PEAK_FP8_TFLOPS if fp8 else PEAK_FP16_TFLOPS
     mixed = PEAK_MIXED_TFLOPS if fp8 else PEAK_FP16_TFLOPS
-    return {"n_valid": n, "n_query": R, "heads": H, "precision": "fp8_e4m3" if fp8 else "fp16",
+    return {"n_valid": n if not w.lengths else list(ns), "n_query": R, "heads": H, "batch": w.batch,
+            "precision": "fp8_e4m3" if fp8 else "fp16",
             "scale": ["none", "log", "gated_log"][w.scale_mode], "warmup": warm, "steps": steps,
             "ms_per_step": round(sec * 1e3, 4),
-            "TFLOP_per_s_step": round((ctx_flops + 4.0 * R * n * D * H) / sec / 1e12, 1),
+            "TFLOP_per_s_step": round((ctx_flops + q_flops) / sec / 1e12, 1),
             "context_kernel_ms": round(ctx_ms, 4), "context_TFLOP_per_s": round(achieved, 1),
             "peak": peak, "frac": round(achieved / peak, 4),
             "peak_mixed": round(mixed, 1), "frac_mixed": round(achieved / mixed, 4)}
@@ -435,7 +440,7 @@ def main() -> int:
                     help="skip measuring the sustained MFMA and HBM-read peaks")
     ap.add_argument("--no-other", action="store_true",
                     help="skip the 128K FP8 and 16K FP16 model calls")
-    ap.add_argument("--other-workloads", default="ctx128k_fp8,ctx16k_log_fp16,ctx16k_gated_fp16")
+    ap.add_argument("--other-workloads", default="ctx128k_fp8,ctx16k_log_fp16,ctx16k_gated_fp16,ragged128k_fp8")
     ap.add_argument("--cpu-sample-rows", type=int, default=384)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (3 times) and exit; "

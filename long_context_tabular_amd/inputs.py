@@ -75,7 +75,8 @@ class Workload:
 
 # The five workloads: tiny FP16, 16K LogScale/GatedLogScale FP16, 128K FP8,
 # a 512K cached FP8 prediction and a full 512K FP8 model call with a ragged
-# (masked) context tail.
+# (masked) context tail; and a ragged pair of 128K/64K FP8 contexts in one
+# launch (per-batch lengths).
 WORKLOADS: Dict[str, Workload] = {
     "tiny_fp16": Workload(
         name="tiny_fp16", seed=0, n_pad=1024, n_valid=1024, n_query=64, heads=4,
@@ -97,6 +98,11 @@ WORKLOADS: Dict[str, Workload] = {
         scale_mode=SCALE_GATED_LOG, precision=PREC_FP8_E4M3, outliers=True,
         query_batches=(128, 1024),
         description="1,024 GatedLogScale queries against a resident 524,288-row FP8 cache"),
+    "ragged128k_fp8": Workload(
+        name="ragged128k_fp8", seed=5, batch=2, n_pad=131072, n_valid=131072, n_query=1024,
+        precision=PREC_FP8_E4M3, outliers=True, nan_tail=True, lengths=(131072, 65537),
+        description="two contexts of 131,072 and 65,537 rows in one launch (rows past each "
+                    "length masked) + 1,024 queries per element, FP8 e4m3"),
     "model512k_fp8_log": Workload(
         name="model512k_fp8_log", seed=4, n_pad=524288, n_valid=523288, n_query=1024,
         scale_mode=SCALE_LOG, precision=PREC_FP8_E4M3, outliers=True, nan_tail=True,

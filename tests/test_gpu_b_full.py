@@ -2,7 +2,8 @@
 benchmark uses.  Outputs are compared element by element with the float64
 oracle (each row against all n keys): every row of the tiny and the 16K
 workloads, every query row of the others, and seeded samples of context rows
-(2,048 at 128K; 1,024 valid rows, including the first and last 8, at 512K);
+(2,048 at 128K; 1,024 valid rows, including the first and last 8, at 512K
+and per element of the ragged 128K + 64K pair);
 FP8 codes and scales bitwise; and the bitwise invariants at full size.  The
 oracle runs on the host's cores, one head and a share of the rows per
 thread."""
@@ -116,6 +117,42 @@ def test_full_model512k_fp8_log():
     assert info["n_valid"] == 523288 and info["length_scalar"] == r.oracle.L32
     assert np.all(out[0, w.n_valid:] == 0)
     _check(r, out, oq.cpu().numpy(), gen.sample_rows(w.n_valid, 1024, w.seed), np.arange(1024))
+
+
+@pytest.mark.timeout(600)
+def test_full_ragged128k_fp8():
+    """The ragged pair the benchmark times (131,072 and 65,537 valid rows of
+    131,072 in one fit and one query launch, FP8, outliers, NaN past each
+    length): codes and scales bitwise, 1,024 sampled context rows of each
+    element (its first and last 8 included) and all 1,024 queries of each,
+    against all of that element's keys; the masked rows of the short element
+    exactly zero."""
+    import torch
+    w = gen.WORKLOADS["ragged128k_fp8"]
+    r = Run(w)
+    say("full ragged128k_fp8")
+    cache, out = r.fit(out_ctx=True)
+    oq = r.query(cache)
+    torch.cuda.synchronize()
+    k, v, sc = B.sdm_icl_attn_cache_export(cache)
+    n_b, _ = B.sdm_icl_attn_cache_lengths(cache)
+    cache.release()
+    assert list(n_b) == [131072, 65537]
+    o = r.oracle
+    np.testing.assert_array_equal(sc, o.scales)
+    for b, n in enumerate((131072, 65537)):
+        np.testing.assert_array_equal(k[b, :, :n], o.k_codes_b[b])
+        np.testing.assert_array_equal(v[b, :, :n], o.v_codes_b[b])
+        assert not np.any(k[b, :, n:]) and not np.any(v[b, :, n:])
+    out, oq = out.cpu().numpy(), oq.cpu().numpy()
+    assert not np.any(out[1, 65537:])
+    tol = TOL[w.precision]
+    for b, n in enumerate((131072, 65537)):
+        rows = gen.sample_rows(n, 1024, 70 + b)
+        e_c = norm_err(out[b, rows].astype(np.float64), r.ref_context(rows, b=b))
+        e_q = norm_err(oq[b].astype(np.float64), r.ref_query(np.arange(1024), b=b))
+        say(f"  b={b} (n={n}): context err {e_c:.3e}, query err {e_q:.3e} (tol {tol})")
+        assert e_c <= tol and e_q <= tol
 
 
 @pytest.mark.timeout(600)
